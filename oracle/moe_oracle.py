@@ -1,0 +1,437 @@
+"""CPU oracle for the DeepSeekMoE layer forward (DeepSeek-V3 shape).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (the HIP library and its Python binding) never does, and this
+module shares no code with it.
+
+It is the plain, slow definition of what the layer computes, in numpy float64
+(float32 where the method fixes float32: the router logits, the affinities,
+the biased selection scores and the bias itself).  Sources, cited by page title
+and section:
+
+  [V3]   "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token"
+         (PaperTrace close reading of the DeepSeek-V3 technical report)
+         §1.1 shapes; §1.3 sigmoid gating and node-limited routing (Eq 12,
+         13, 15); §1.4 auxiliary-loss-free balancing (Eq 16); §2.2 FP8
+         fine-grained quantisation; §5.1 deployment (shared expert as an
+         always-selected expert).
+  [DEP]  "DeepSeek-V3 MoE cost and deployment" audit page (FP8 weight release).
+
+The display equations of [V3] are missing from the extracted text; every
+formula below is rebuilt from the surrounding prose, and each reading taken
+where the prose is silent is named in the docstring that uses it.
+
+Parity status of each function (what pins it in tests/test_oracle_*.py):
+  router_affinity       pinned (loop brute force; sigmoid vs scipy.expit)
+  select_experts        pinned (subset-enumeration brute force; plain top-K
+                        special case; group containment; bias invariants)
+  gate_values           pinned (sum-to-one; bias-independence)
+  permute               pinned (per-expert brute-force listing; bincount)
+  expert_ffn / forward  pinned for the FFN and combine structure (scalar
+                        triple-loop brute force, shared-only and single-expert
+                        special cases); layer output VALUES at V3 size are
+                        otherwise parity unpinned: the pages print no worked
+                        example of the layer.
+  bias_update           pinned (rule worked by hand from §1.4, golden file)
+  e4m3_* / quantize_1x128  pinned (all 256 codes; torch float8_e4m3fn)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, Dict, Optional, Sequence
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+NEAR_TIE = 1e-6   # gap below which a selection is flagged, in biased score units
+
+
+# ----------------------------------------------------------------------------
+# inputs
+# ----------------------------------------------------------------------------
+
+def lift(a) -> np.ndarray:
+    """Exact lift of a float32 / bfloat16 array (numpy or torch CPU) to float64."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu")
+            if a.dtype == torch.bfloat16:
+                a = a.to(torch.float32)          # exact
+            a = a.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------
+# step 1: router affinities ([V3] §1.3, Eq 15)
+# ----------------------------------------------------------------------------
+
+def router_affinity(x64: np.ndarray, wr64: np.ndarray):
+    """Logits and sigmoid affinities of every token for every routed expert.
+
+    The affinity of token t for expert i is the logistic sigmoid of the dot
+    product of the token with the expert's centroid (a column of the router
+    weight), [V3] §1.3 Eq 15.  The logit is formed as a float64 dot product and
+    rounded once to float32; the sigmoid is evaluated in float64 on that
+    float32 logit and rounded to float32 (the method works in float32).
+
+    Returns (L float32 [T][E], s float32 [T][E]).
+    """
+    L = (x64 @ wr64).astype(F32)
+    Ld = L.astype(F64)
+    s = (1.0 / (1.0 + np.exp(-Ld))).astype(F32)
+    return L, s
+
+
+# ----------------------------------------------------------------------------
+# steps 2-3: node-limited selection and gates ([V3] §1.3, §1.4)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Routing:
+    idx: np.ndarray        # [T][K] int32, ascending expert id
+    gate: np.ndarray       # [T][K] float32, sums to 1 per token
+    z: np.ndarray          # [T][E] float32 biased scores s + b
+    group_score: np.ndarray  # [T][G] float32
+    groups: np.ndarray     # [T][topk_groups] int32 kept groups (rank order)
+    egap: np.ndarray       # [T] float64: z of K-th minus (K+1)-th eligible expert
+    ggap: np.ndarray       # [T] float64: kept-group score minus best dropped one
+    flagged: np.ndarray    # [T] bool: min(egap, ggap) < NEAR_TIE
+
+
+def biased_scores(s32: np.ndarray, b32: np.ndarray) -> np.ndarray:
+    """Selection score z = s + b in float32.
+
+    [V3] §1.4 (Eq 16): the per-expert bias enters the ranking only; it is added
+    to the sigmoid affinity (after the sigmoid), in float32.
+    """
+    return (s32.astype(F32) + b32.astype(F32)[None, :]).astype(F32)
+
+
+def group_scores(z32: np.ndarray, n_groups: int, group_topn: int) -> np.ndarray:
+    """Score of each expert group: sum of its ``group_topn`` largest biased scores.
+
+    [V3] §1.3: experts are spread evenly over the nodes and each node is ranked
+    by the sum of its top K_r/M = 2 affinities.  Readings: groups are
+    contiguous blocks of E/G expert ids; the summed scores are the biased ones
+    (s + b), since the ranking of §1.4 uses s + b; the float32 sum is taken
+    from the largest value down.
+    """
+    T, E = z32.shape
+    zg = z32.reshape(T, n_groups, E // n_groups)
+    top = -np.sort(-zg, axis=2)[:, :, :group_topn]
+    gs = top[:, :, 0].astype(F32)
+    for j in range(1, group_topn):
+        gs = (gs + top[:, :, j]).astype(F32)
+    return gs
+
+
+def select_experts(s32: np.ndarray, b32: np.ndarray, n_groups: int, topk_groups: int,
+                   topk: int, group_topn: int = 2) -> Routing:
+    """Node-limited top-K selection with the loss-free bias, and the gates.
+
+    [V3] §1.3: rank the groups by their group score, keep the best
+    ``topk_groups`` (4 of 8 for V3), then take the ``topk`` (8) experts with the
+    largest scores among the kept groups' experts only.  [V3] §1.4: the ranking
+    uses z = s + b.  Exact ties go to the lower group / expert index.  The
+    chosen experts are listed in ascending id.
+    """
+    T, E = s32.shape
+    per = E // n_groups
+    z = biased_scores(s32, b32)
+    gs = group_scores(z, n_groups, group_topn)
+    gorder = np.argsort(-gs, axis=1, kind="stable")        # ties: lower index first
+    groups = gorder[:, :topk_groups].astype(np.int32)
+    eligible = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(eligible, groups.astype(np.int64), True, axis=1)
+    elig_e = np.repeat(eligible, per, axis=1)                # [T][E]
+    masked = np.where(elig_e, z.astype(F64), -np.inf)
+    eorder = np.argsort(-masked, axis=1, kind="stable")
+    idx = np.sort(eorder[:, :topk], axis=1).astype(np.int32)
+
+    zs = np.take_along_axis(masked, eorder, axis=1)
+    n_elig = topk_groups * per
+    egap = zs[:, topk - 1] - zs[:, topk] if n_elig > topk else np.full(T, np.inf)
+    if topk_groups < n_groups:
+        gss = np.take_along_axis(gs.astype(F64), gorder, axis=1)
+        ggap = gss[:, topk_groups - 1] - gss[:, topk_groups]
+    else:
+        ggap = np.full(T, np.inf)
+    flagged = np.minimum(egap, ggap) < NEAR_TIE
+    gate = gate_values(s32, idx)
+    return Routing(idx=idx, gate=gate, z=z, group_score=gs, groups=groups,
+                   egap=egap, ggap=ggap, flagged=flagged)
+
+
+def gate_values(s32: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Gates of the chosen experts: their unbiased affinities renormalised to sum to 1.
+
+    [V3] §1.3 (Eq 13): after the top-K choice the K affinities are normalised
+    among themselves; [V3] §1.4: the bias is not part of the gate.  Computed in
+    float64 from the float32 affinities and rounded to float32.
+    """
+    sel = np.take_along_axis(s32.astype(F64), idx.astype(np.int64), axis=1)
+    return (sel / sel.sum(axis=1, keepdims=True)).astype(F32)
+
+
+# ----------------------------------------------------------------------------
+# step 4: permutation by expert ([V3] §1.3: no token is dropped)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Perm:
+    counts: np.ndarray   # [E] int32
+    offsets: np.ndarray  # [E+1] int32
+    perm: np.ndarray     # [T*K] int32 token id of each expert-ordered row
+    slot: np.ndarray     # [T*K] int32 expert-ordered row of assignment t*K+k
+
+
+def permute(idx: np.ndarray, n_experts: int) -> Perm:
+    """Group the token-expert assignments by expert, keeping token order.
+
+    Every assignment is kept (no dropping, [V3] §1.3).  Assignments are
+    enumerated token-major (a = t*K + k); a stable sort by expert id lists the
+    rows of each expert in ascending token order.
+    """
+    T, K = idx.shape
+    e_of = idx.reshape(-1).astype(np.int64)
+    order = np.argsort(e_of, kind="stable")
+    counts = np.bincount(e_of, minlength=n_experts).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    slot = np.empty(T * K, dtype=np.int32)
+    slot[order] = np.arange(T * K, dtype=np.int32)
+    return Perm(counts=counts, offsets=offsets, perm=(order // K).astype(np.int32), slot=slot)
+
+
+# ----------------------------------------------------------------------------
+# step 5: SwiGLU experts and the gated combine ([V3] §1.1, §1.3 Eq 12)
+# ----------------------------------------------------------------------------
+
+def route(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, *, n_groups: int, topk_groups: int,
+          topk: int, group_topn: int = 2):
+    """Steps 1-4 only: affinities, selection, gates and the expert permutation.
+
+    Returns (L, s, Routing, Perm).
+    """
+    L, s = router_affinity(x64, wr64)
+    r = select_experts(s, b32, n_groups, topk_groups, topk, group_topn)
+    return L, s, r, permute(r.idx, wr64.shape[1])
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v / (1.0 + np.exp(-v))
+
+
+def expert_ffn(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on the rows of X, float64.
+
+    [V3] §1.1: an expert is a SwiGLU block of three matrices
+    (hidden -> intermediate -> hidden).  Reading: H = SiLU(X W_gate^T) * (X W_up^T),
+    Y = H W_down^T with SiLU(v) = v * sigmoid(v); W_gate, W_up are
+    [inter][hidden] and W_down is [hidden][inter].
+    """
+    G = X @ wg.T
+    U = X @ wu.T
+    return (silu(G) * U) @ wd.T
+
+
+ExpertSource = Callable[[int], Dict[str, np.ndarray]]
+
+
+def dequant_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Weights stored as e4m3 codes with one float32 scale per 128x128 block, as float64."""
+    v = e4m3_decode(codes)
+    R, C = v.shape
+    return (v.reshape(R // 128, 128, C // 128, 128) * scales.astype(F64)[:, None, :, None]).reshape(R, C)
+
+
+def expert_f64(w: Dict[str, np.ndarray]):
+    """(W_gate, W_up, W_down) of one expert as float64 (e4m3 codes dequantised)."""
+    if "s_gate" in w:
+        return (dequant_blocks(w["w_gate"], w["s_gate"]), dequant_blocks(w["w_up"], w["s_up"]),
+                dequant_blocks(w["w_down"], w["s_down"]))
+    return lift(w["w_gate"]), lift(w["w_up"]), lift(w["w_down"])
+
+
+@dataclass
+class ForwardResult:
+    y: np.ndarray          # [n_tokens][H] float64 MoE branch (+ residual if given)
+    tokens: np.ndarray     # token ids the rows of y belong to
+    routing: Routing
+    perm: Perm
+
+
+def forward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: ExpertSource, *,
+            n_groups: int, topk_groups: int, topk: int, group_topn: int = 2, n_shared: int = 1,
+            tokens: Optional[Sequence[int]] = None, residual: Optional[np.ndarray] = None,
+            act_quant: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> ForwardResult:
+    """The MoE layer output for every token (or for ``tokens`` only).
+
+    [V3] §1.3 Eq 12: the output is the shared expert's FFN output plus the
+    gate-weighted sum of the chosen routed experts' FFN outputs (plus the
+    residual u_t, which is added only when ``residual`` is given).  The shared
+    expert is always applied with weight 1 outside the gate normalisation
+    ([V3] §5.1 treats it as a ninth, always-selected expert).  Routing always
+    covers all T tokens (the permutation depends on the whole batch); expert
+    FFNs are evaluated only for the requested tokens.
+
+    ``experts(e)`` returns expert e's weights (routed 0..E-1, shared = E).
+    ``act_quant`` (optional) maps a float64 activation matrix to its quantised
+    value; it is applied to the expert inputs and to the SwiGLU output.
+    """
+    T = x64.shape[0]
+    E = wr64.shape[1]
+    L, s = router_affinity(x64, wr64)
+    r = select_experts(s, b32, n_groups, topk_groups, topk, group_topn)
+    p = permute(r.idx, E)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    xin = x64[tok]
+    if act_quant is not None:
+        xin = act_quant(xin)
+    y = np.zeros((len(tok), x64.shape[1]), dtype=F64)
+
+    def ffn(w, X):
+        wg, wu, wd = expert_f64(w)
+        if act_quant is None:
+            return expert_ffn(X, wg, wu, wd)
+        Hq = act_quant((silu(X @ wg.T) * (X @ wu.T)).astype(F32).astype(F64))
+        return Hq @ wd.T
+
+    # routed experts in ascending id, each on the requested tokens that chose
+    # it, so every token accumulates its K terms in ascending expert order
+    sel = r.idx[tok]
+    for e in sorted(set(int(v) for v in sel.reshape(-1))):
+        jj, kk = np.nonzero(sel == e)
+        Y = ffn(experts(e), xin[jj])
+        y[jj] += r.gate[tok[jj], kk].astype(F64)[:, None] * Y
+    for sh in range(n_shared):
+        y += ffn(experts(E + sh), xin)
+    if residual is not None:
+        y += lift(residual)[tok]
+    return ForwardResult(y=y, tokens=tok, routing=r, perm=p)
+
+
+# ----------------------------------------------------------------------------
+# step 6: auxiliary-loss-free bias update ([V3] §1.4)
+# ----------------------------------------------------------------------------
+
+def bias_update(b32: np.ndarray, counts: np.ndarray, T: int, K: int, gamma: float) -> np.ndarray:
+    """One loss-free balancing step on the bias.
+
+    [V3] §1.4: at the end of a step the load of each expert over the whole
+    batch is counted; an overloaded expert's bias drops by gamma and an
+    underloaded one's rises by gamma (a sign update).  Reading: the mean load
+    is T*K/E; overloaded means count > mean, underloaded count < mean, and an
+    expert at exactly the mean keeps its bias.  Compared as count*E vs T*K in
+    integers; the update is one float32 add.
+    """
+    b = np.asarray(b32, dtype=F32).copy()
+    E = b.shape[0]
+    c = np.asarray(counts, dtype=np.int64)
+    g = F32(gamma)
+    over = c * E > T * K
+    under = c * E < T * K
+    b[over] = (b[over] - g).astype(F32)
+    b[under] = (b[under] + g).astype(F32)
+    return b
+
+
+def load_ratio(counts: np.ndarray) -> float:
+    """Max over mean per-expert load."""
+    c = np.asarray(counts, dtype=F64)
+    return float(c.max() / c.mean())
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 fine-grained quantisation ([V3] §2.2)
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each OCP E4M3FN code (1 sign, 4 exponent bits biased by 7, 3 mantissa bits).
+
+    Exponent field 0 holds subnormals m * 2^-9; field 15 with mantissa 7 is NaN
+    (the format has no infinities).
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = (c & 0x7).astype(F64)
+    val = np.where(ef == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(ef.astype(F64) - 7.0))
+    val = np.where((ef == 15) & ((c & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_quantize(v) -> np.ndarray:
+    """Round float32 values to E4M3FN codes: nearest, ties to even, saturating at +-448.
+
+    Values below the smallest subnormal half-step round to signed zero.
+    """
+    a = np.asarray(v, dtype=F64)
+    sign = (np.signbit(a)).astype(np.int64) << 7
+    mag = np.abs(a)
+    # binade exponent for normals (min normal 2^-6); spacing 2^(e-3); subnormal spacing 2^-9
+    _, ex = np.frexp(np.where(mag > 0, mag, 1.0))    # mag = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    step = np.exp2(e.astype(F64) - 3.0)
+    q = np.round(mag / step) * step                   # np.round: half to even
+    q = np.minimum(q, E4M3_MAX)
+    # encode
+    _, qex = np.frexp(np.where(q > 0, q, 1.0))
+    qe = qex - 1
+    normal = q >= 2.0 ** -6
+    ef = np.where(normal, qe + 7, 0)
+    mant = np.where(normal, np.round((q / np.exp2(qe.astype(F64)) - 1.0) * 8.0),
+                    np.round(q / 2.0 ** -9))
+    code = sign | (ef.astype(np.int64) << 3) | mant.astype(np.int64)
+    return code.astype(np.uint8)
+
+
+def quantize_1x128(a: np.ndarray):
+    """Per-row, per-128-column online quantisation of an activation matrix.
+
+    [V3] §2.2: activations are grouped in 1x128 tiles (one token, 128
+    channels); each tile's scale comes from its current max-abs value and the
+    values are stored as E4M3.  Reading: scale = amax / 448 in float32 (1 for an
+    all-zero tile); code = RNE(v / scale) computed in float32.
+
+    Returns (codes uint8 [R][C], scales float32 [R][C/128]).
+    """
+    a32 = np.asarray(a, dtype=F32)
+    R, C = a32.shape
+    t = a32.reshape(R, C // 128, 128)
+    amax = np.abs(t).max(axis=2)
+    scale = np.where(amax > 0, (amax / F32(448.0)).astype(F32), F32(1.0)).astype(F32)
+    ratio = (t / scale[:, :, None]).astype(F32)
+    return e4m3_quantize(ratio).reshape(R, C), scale
+
+
+def dequantize_1x128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    R, C = codes.shape
+    return (e4m3_decode(codes).reshape(R, C // 128, 128) * scales.astype(F64)[:, :, None]).reshape(R, C)
+
+
+def fake_quant_1x128(a: np.ndarray) -> np.ndarray:
+    """Quantise then dequantise (float64 result): the emulation mode's activation map."""
+    q, s = quantize_1x128(np.asarray(a, dtype=F64).astype(F32))
+    return dequantize_1x128(q, s)
+
+
+# ----------------------------------------------------------------------------
+# error metric
+# ----------------------------------------------------------------------------
+
+def max_row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of ||y_t - ref_t||_2 / ||ref_t||_2."""
+    y = np.asarray(y, dtype=F64)
+    ref = np.asarray(ref, dtype=F64)
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    return float(np.max(num / np.maximum(den, 1e-300)))

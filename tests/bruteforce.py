@@ -1,0 +1,78 @@
+"""Brute-force reference computations for tiny inputs (pure Python loops).
+
+Independent of oracle/: written from the method's description by enumeration
+instead of sorting, for use as pins of the oracle on tiny sizes.
+"""
+import itertools
+import math
+
+import numpy as np
+
+
+def logits_loop(x, wr):
+    """L[t][e] = sum_h x[t][h] * wr[h][e] by an explicit float64 loop, rounded to float32."""
+    T, H = x.shape
+    E = wr.shape[1]
+    out = np.zeros((T, E), dtype=np.float32)
+    for t in range(T):
+        for e in range(E):
+            acc = 0.0
+            for h in range(H):
+                acc += float(x[t, h]) * float(wr[h, e])
+            out[t, e] = np.float32(acc)
+    return out
+
+
+def select_enumerate(z, n_groups, topk_groups, topk, group_topn=2):
+    """Node-limited selection by enumeration of subsets, for one token.
+
+    z: float32 [E] biased scores.  Group score = the largest sum over all
+    ``group_topn``-subsets of the group's experts.  The kept groups are the
+    ``topk_groups``-subset of groups with the largest total group score; the
+    chosen experts are the ``topk``-subset of the kept groups' experts with the
+    largest total score.  Equal totals break toward the lexicographically
+    smallest index tuple.  Sums are exact (float64 of float32 values).
+    """
+    E = len(z)
+    per = E // n_groups
+    zf = [float(v) for v in z]
+    gscore = []
+    for g in range(n_groups):
+        members = range(g * per, (g + 1) * per)
+        best = max(sum(zf[i] for i in c) for c in itertools.combinations(members, group_topn))
+        gscore.append(best)
+    best_g, best_gs = None, -math.inf
+    for c in itertools.combinations(range(n_groups), topk_groups):
+        tot = sum(gscore[g] for g in c)
+        if tot > best_gs:
+            best_g, best_gs = c, tot
+    elig = [i for g in best_g for i in range(g * per, (g + 1) * per)]
+    best_e, best_es = None, -math.inf
+    for c in itertools.combinations(sorted(elig), topk):
+        tot = sum(zf[i] for i in c)
+        if tot > best_es:
+            best_e, best_es = c, tot
+    return sorted(best_e), sorted(best_g), gscore
+
+
+def swiglu_loop(xv, wg, wu, wd):
+    """One token through one SwiGLU expert by scalar loops.
+
+    h_j = silu(sum_k wg[j][k] x_k) * (sum_k wu[j][k] x_k); y_i = sum_j wd[i][j] h_j.
+    """
+    I, H = wg.shape
+    h = [0.0] * I
+    for j in range(I):
+        g = 0.0
+        u = 0.0
+        for k in range(H):
+            g += float(wg[j, k]) * float(xv[k])
+            u += float(wu[j, k]) * float(xv[k])
+        h[j] = g / (1.0 + math.exp(-g)) * u
+    y = [0.0] * H
+    for i in range(H):
+        acc = 0.0
+        for j in range(I):
+            acc += float(wd[i, j]) * h[j]
+        y[i] = acc
+    return np.array(y)

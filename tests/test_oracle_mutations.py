@@ -1,0 +1,113 @@
+"""Each plausible mistake planted in the oracle (on the CPU) must fail a pin.
+
+The mistakes are patched into the oracle module for the duration of one call
+of an existing pin test; the test then must raise AssertionError.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as M
+from tests import test_oracle_ffn as TF
+from tests import test_oracle_fp8 as T8
+from tests import test_oracle_routing as TR
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(M, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+_orig = {n: getattr(M, n) for n in ("group_scores", "biased_scores", "gate_values", "permute",
+                                     "expert_ffn", "bias_update", "router_affinity",
+                                     "e4m3_quantize", "select_experts")}
+
+
+def m_group_top1(z, n_groups, group_topn):
+    return _orig["group_scores"](z, n_groups, 1)
+
+
+def m_no_bias(s, b):
+    return s.astype(np.float32)
+
+
+def m_gate_biased(s, idx):
+    return _orig["gate_values"]((s + np.float32(0.1)).astype(np.float32), idx)
+
+
+def m_gate_all_experts(s, idx):
+    sel = np.take_along_axis(s.astype(np.float64), idx.astype(np.int64), axis=1)
+    return (sel / s.astype(np.float64).sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def m_perm_reversed(idx, E):
+    p = _orig["permute"](idx, E)
+    for e in range(E):
+        a, b = p.offsets[e], p.offsets[e + 1]
+        p.perm[a:b] = p.perm[a:b][::-1].copy()
+    return p
+
+
+def m_ffn_swapped(X, wg, wu, wd):
+    return _orig["expert_ffn"](X, wu, wg, wd)
+
+
+def m_bias_sign(b, counts, T, K, gamma):
+    return _orig["bias_update"](b, counts, T, K, -gamma)
+
+
+def m_bias_ge(b, counts, T, K, gamma):
+    bb = np.asarray(b, np.float32).copy()
+    c = np.asarray(counts) * len(bb)
+    bb[c >= T * K] -= np.float32(gamma)
+    bb[c < T * K] += np.float32(gamma)
+    return bb.astype(np.float32)
+
+
+def m_sigmoid_sign(x, wr):
+    L, s = _orig["router_affinity"](x, wr)
+    return L, (1.0 / (1.0 + np.exp(L.astype(np.float64)))).astype(np.float32)
+
+
+def m_round_away(v):
+    a = np.asarray(v, np.float64)
+    return _orig["e4m3_quantize"](a + np.sign(a) * np.abs(a) * 2.0 ** -20)
+
+
+def m_select_ascending(s, b, n_groups, topk_groups, topk, group_topn=2):
+    return _orig["select_experts"](-s, -b, n_groups, topk_groups, topk, group_topn)
+
+
+CASES = [
+    ("group_scores", m_group_top1, TR.test_selection_matches_subset_enumeration, (0,)),
+    ("biased_scores", m_no_bias, TR.test_large_bias_forces_and_excludes_experts, ()),
+    ("gate_values", m_gate_biased, TR.test_bias_changes_selection_not_gate_values, ()),
+    ("gate_values", m_gate_all_experts, TR.test_gates_sum_to_one_and_are_positive, ()),
+    ("permute", m_perm_reversed, TR.test_permutation_matches_per_expert_listing, ()),
+    ("expert_ffn", m_ffn_swapped, TF.test_expert_ffn_matches_scalar_loops, ()),
+    ("bias_update", m_bias_sign, TR.test_bias_update_golden_example, ()),
+    ("bias_update", m_bias_ge, TR.test_bias_update_golden_example, ()),
+    ("router_affinity", m_sigmoid_sign, TR.test_sigmoid_matches_scipy_expit, ()),
+    ("e4m3_quantize", m_round_away, T8.test_midpoints_round_to_even_and_saturate, ()),
+    ("select_experts", m_select_ascending, TR.test_plain_topk_when_all_groups_kept, ()),
+]
+
+
+@pytest.mark.parametrize("name,fn,pin,args", CASES, ids=[f"{c[0]}:{c[1].__name__}" for c in CASES])
+def test_planted_mistake_fails_a_pin(monkeypatch, name, fn, pin, args):
+    _patch(monkeypatch, name, fn)
+    with pytest.raises(AssertionError):
+        pin(*args)
+
+
+def test_dropped_shared_expert_fails_combine_pin(monkeypatch):
+    orig_forward = M.forward
+
+    def no_shared(*a, **kw):
+        kw["n_shared"] = 0
+        return orig_forward(*a, **kw)
+
+    monkeypatch.setattr(M, "forward", no_shared)
+    monkeypatch.setattr(oracle, "forward", no_shared)
+    with pytest.raises(AssertionError):
+        TF.test_layer_output_matches_bruteforce_combine()
