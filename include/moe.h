@@ -1,0 +1,196 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) DeepSeekMoE layer-forward library.
+ *
+ * What the library computes is the MoE layer of DeepSeek-V3 as described on
+ * the page "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token" (a close reading
+ * of the DeepSeek-V3 technical report):
+ *   §1.3 (Eq 15)  router affinities s = sigmoid(x · W_r), float32;
+ *   §1.3 / §1.4   node-limited selection: experts form n_groups contiguous
+ *                 groups, a group's score is the sum of its group_topn largest
+ *                 biased scores z = s + b, the topk_groups best groups are kept
+ *                 and the topk largest z among their experts are chosen;
+ *   §1.3 (Eq 13)  gates: the chosen experts' unbiased s renormalised to sum 1;
+ *   §1.3          no token is dropped; tokens are grouped by expert;
+ *   §1.1          every expert is a SwiGLU FFN hidden -> inter -> hidden;
+ *   §1.3 (Eq 12)  output = shared experts' FFN + sum_k gate_k · FFN_{e_k};
+ *   §1.4          loss-free bias step: b_e -= gamma if expert e's load is
+ *                 above the mean, b_e += gamma if below, unchanged if equal;
+ *   §2.2          FP8 (E4M3) weights with one float32 scale per 128x128 block,
+ *                 activations quantised online per 1x128 slice, float32
+ *                 accumulation with the scales applied per 128-wide K block.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to GPU memory of the current
+ *    HIP device; they are owned by the caller, which keeps them alive until the
+ *    enqueued work has finished.  The library allocates no device memory and
+ *    keeps no pointer after a call returns.  Struct arguments (moe_cfg,
+ *    moe_routing, moe_experts) are host memory, read during the call only.
+ *  - All GPU work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *    default stream) without synchronising the host.  The return status covers
+ *    argument validation and launch errors; a fault while the kernels run is
+ *    reported by the caller's next synchronisation.
+ *  - On a validation error nothing is launched and no output is written.
+ *  - T == 0 returns MOE_OK and launches nothing.
+ *  - Results are deterministic: the same inputs give bitwise identical outputs
+ *    (no floating-point atomics; integer atomics only where the result does
+ *    not depend on their order).
+ *  - Calls are thread-safe when they use distinct workspaces; calls sharing a
+ *    workspace must be ordered on one stream.
+ *  - Non-finite inputs are not checked; the results are then undefined.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum moe_dtype {
+  MOE_F32 = 0,   /* IEEE binary32 */
+  MOE_BF16 = 1,  /* bfloat16 */
+  MOE_E4M3 = 2   /* OCP FP8 E4M3FN codes (1 byte), weights only */
+};
+
+/* status codes */
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,       /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,      /* inconsistent or unsupported sizes */
+  MOE_ERR_DTYPE = -3,      /* unsupported dtype combination */
+  MOE_ERR_WORKSPACE = -4,  /* workspace NULL or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -5,        /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_DEVICE = -6      /* the current device is not a gfx950 GPU */
+};
+
+/*
+ * Layer shape.  V3: hidden 7168, inter 2048, n_experts 256, n_groups 8,
+ * topk_groups 4, topk 8, group_topn 2, n_shared 1.
+ * Constraints (else MOE_ERR_SHAPE):
+ *   n_experts % n_groups == 0, n_experts <= 512, n_groups <= 64,
+ *   1 <= group_topn <= min(4, n_experts / n_groups), 1 <= topk_groups <= n_groups,
+ *   1 <= topk <= min(32, topk_groups * n_experts / n_groups),
+ *   n_shared in {0, 1}, hidden % 128 == 0, inter % 128 == 0,
+ *   T * (topk + n_shared) < 2^31.
+ * Dtypes (else MOE_ERR_DTYPE): (act, w) = (F32, F32), (BF16, BF16) or (BF16, E4M3).
+ */
+typedef struct moe_cfg {
+  int32_t hidden;       /* H: model width */
+  int32_t inter;        /* I: expert intermediate width */
+  int32_t n_experts;    /* E: routed experts */
+  int32_t n_groups;     /* G: expert groups (nodes in the pages' deployment) */
+  int32_t topk_groups;  /* groups kept per token */
+  int32_t topk;         /* K: routed experts per token */
+  int32_t group_topn;   /* biased scores summed per group */
+  int32_t n_shared;     /* S: shared experts, always applied with weight 1 */
+  int32_t act_dtype;    /* moe_dtype of x, residual and y */
+  int32_t w_dtype;      /* moe_dtype of the expert weights */
+} moe_cfg;
+
+/*
+ * Routing results (device pointers, caller-allocated).  Layouts:
+ *   topk_idx  int32 [T][K]  chosen expert ids, ascending per token
+ *   topk_gate float [T][K]  gates, same order, each row sums to 1
+ *   counts    int32 [E]     assignments per expert (sum = T*K)
+ *   offsets   int32 [E+1]   exclusive prefix sum of counts
+ *   perm      int32 [T*K]   token id of each expert-ordered row: rows
+ *                           offsets[e] .. offsets[e+1]-1 list the tokens that
+ *                           chose expert e in ascending token order
+ *   slot      int32 [T*K]   row of assignment t*K+k in that order
+ *   tie_gap   float [T]     may be NULL: min over the token of (K-th minus
+ *                           (K+1)-th eligible biased score) and (kept minus
+ *                           best dropped group score); < 1e-6 marks a near-tie
+ */
+typedef struct moe_routing {
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot;
+  float* tie_gap;
+} moe_routing;
+
+/*
+ * Expert weights (device pointers).  Routed experts are 0..E-1; the shared
+ * expert is index E.  Row-major layouts:
+ *   w_gate, w_up  [E+S][I][H]   element type w_dtype
+ *   w_down        [E+S][H][I]
+ *   s_gate, s_up  float [E+S][I/128][H/128]   (E4M3 only, else ignored)
+ *   s_down        float [E+S][H/128][I/128]   (E4M3 only, else ignored)
+ * For E4M3 the weight value is code * scale of its 128x128 block.
+ */
+typedef struct moe_experts {
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+} moe_experts;
+
+/* Workspace bytes that moe_route / moe_forward need for T tokens (0 on a bad cfg). */
+size_t moe_workspace_bytes(const moe_cfg* cfg, int64_t T);
+
+/*
+ * Router, node-limited selection, gates and the expert permutation.
+ *   x        device [T][H] act_dtype      token activations
+ *   w_router device float [H][E]          expert centroids as columns
+ *   bias     device float [E]             load-balancing bias (zeros for none)
+ *   out      host struct of device outputs; every field but tie_gap required
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes(cfg, T)
+ */
+int moe_route(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+              const float* bias, const moe_routing* out, void* ws, size_t ws_bytes,
+              void* stream);
+
+/*
+ * The whole layer forward: moe_route followed by the routed and shared
+ * SwiGLU experts and the gated combine.
+ *   residual device [T][H] act_dtype or NULL; when given it is added to y
+ *   y        device [T][H] act_dtype output
+ *   out      NULL (routing kept in the workspace) or as in moe_route
+ * Intermediate activations are rounded to bfloat16 (E4M3 with 1x128 scales
+ * for E4M3 weights; float32 for the F32 configuration) and the combine
+ * accumulates in float32 in ascending expert order, shared expert first.
+ */
+int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+                const float* bias, const moe_experts* w, const void* residual, void* y,
+                const moe_routing* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Loss-free bias step on the loads of one batch.
+ *   counts device int32 [E] (e.g. moe_routing.counts of the step's batch)
+ *   bias   device float [E], updated in place:
+ *          b_e -= gamma if counts_e * E > T * K, b_e += gamma if < , else kept
+ */
+int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float* bias,
+                    float gamma, void* stream);
+
+/*
+ * Kernel timing instrumentation (off by default; not thread-safe).
+ * While enabled, every kernel launch of moe_route / moe_forward /
+ * moe_bias_update is bracketed by a pair of HIP events on the caller's stream.
+ * moe_profile_read waits for the recorded events, adds each pair's elapsed
+ * time to the slot of its kernel, clears the record, and returns the number
+ * of slots (at most n_slots are written to total_ms / launches, which may be
+ * NULL to query the count).  moe_profile_kernel_name names a slot.
+ */
+int moe_profile_enable(int on);
+int moe_profile_read(double* total_ms, int32_t* launches, int n_slots);
+const char* moe_profile_kernel_name(int slot);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+/* ABI version (major * 100 + minor). */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,72 @@
+// Internal helpers of the gfx950 MoE library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte register chunk
+typedef uint16_t bf16_t;  // bfloat16 storage
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+
+MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// round to nearest even; NaN stays NaN
+MOE_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+template <typename T> MOE_DEV float to_f32(T v);
+template <> MOE_DEV float to_f32<float>(float v) { return v; }
+template <> MOE_DEV float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> MOE_DEV T from_f32(float v);
+template <> MOE_DEV float from_f32<float>(float v) { return v; }
+template <> MOE_DEV bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// ---------------------------------------------------------------- math
+
+// logistic sigmoid in float32 with the device library's expf
+MOE_DEV float sigmoidf(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+MOE_DEV float siluf(float v) { return v / (1.0f + expf(-v)); }
+
+// ---------------------------------------------------------------- wave helpers
+
+// (value, index) arg-max over the wave: larger value wins, equal values go to
+// the smaller index.  Every lane returns the winner.
+MOE_DEV void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float ov = __shfl_xor(v, off, kWave);
+    int oi = __shfl_xor(i, off, kWave);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

@@ -1,0 +1,331 @@
+// C ABI of the gfx950 MoE layer library: argument validation, workspace
+// carving and launch sequencing.  Every step of the layer runs in the HIP
+// kernels of route_kernels.hip and gemm_kernels.hip; this file only checks
+// arguments and enqueues them on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::bf16_t;
+
+struct Layout {
+  size_t P, idx, gate, counts, offsets, perm, slot, gap, masks, hist, base, mt_a, mt_b;
+  size_t hst, yst;
+  size_t route_total, total;
+};
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t elem_bytes(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
+
+Layout make_layout(const moe_cfg& c, int64_t T) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
+  const size_t TK = size_t(T) * K;
+  const size_t nc = size_t(moe::perm_chunks(int(T)));
+  L.P = take(size_t(moe::router_ksplit(c.hidden)) * T * E * 4);
+  L.idx = take(TK * 4);
+  L.gate = take(TK * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(TK * 4);
+  L.slot = take(TK * 4);
+  L.gap = take(size_t(T) * 4);
+  L.masks = take(nc * E * 8);
+  L.hist = take(nc * E * 4);
+  L.base = take(nc * E * 4);
+  L.mt_a = take((E + S + 1) * 4);
+  L.mt_b = take((E + S + 1) * 4);
+  L.route_total = off;
+  const size_t rows = TK + S * size_t(T);
+  const size_t es = elem_bytes(c.act_dtype);
+  L.hst = take(rows * I * es);
+  L.yst = take(rows * H * es);
+  L.total = off;
+  return L;
+}
+
+int validate_cfg(const moe_cfg* c) {
+  if (c == nullptr) return MOE_ERR_NULL;
+  if (c->hidden <= 0 || c->inter <= 0 || c->n_experts <= 0 || c->n_groups <= 0) return MOE_ERR_SHAPE;
+  if (c->hidden % 128 != 0 || c->inter % 128 != 0) return MOE_ERR_SHAPE;
+  if (c->n_experts > 512 || c->n_groups > 64 || c->n_experts % c->n_groups != 0) return MOE_ERR_SHAPE;
+  const int gsz = c->n_experts / c->n_groups;
+  if (c->group_topn < 1 || c->group_topn > 4 || c->group_topn > gsz) return MOE_ERR_SHAPE;
+  if (c->topk_groups < 1 || c->topk_groups > c->n_groups) return MOE_ERR_SHAPE;
+  if (c->topk < 1 || c->topk > 32 || c->topk > c->topk_groups * gsz) return MOE_ERR_SHAPE;
+  if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_SHAPE;
+  const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32;
+  const bool bf16 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_BF16;
+  if (!f32 && !bf16) return MOE_ERR_DTYPE;
+  return MOE_OK;
+}
+
+int validate_T(const moe_cfg* c, int64_t T) {
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (T * int64_t(c->topk + c->n_shared) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// gfx950 check, cached per device
+std::atomic<int> g_arch_state[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------- instrumentation
+
+enum Slot { K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_NSLOTS };
+const char* const kSlotNames[K_NSLOTS] = {"router_logits", "select", "permute", "gemm_gate_up",
+                                          "gemm_down", "combine", "bias_update"};
+
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec { int slot; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  double ms[K_NSLOTS] = {0};
+  int n[K_NSLOTS] = {0};
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Prof g_prof;
+
+// run one launcher, bracketed by events when instrumentation is on
+template <typename F> hipError_t timed(int slot, hipStream_t st, F&& f) {
+  if (!g_prof.on) return f();
+  hipEvent_t a = g_prof.get(), b = g_prof.get();
+  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
+  hipEventRecord(a, st);
+  hipError_t err = f();
+  hipEventRecord(b, st);
+  g_prof.recs.push_back({slot, a, b});
+  return err;
+}
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+template <typename P> P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+struct RoutePtrs {
+  int32_t *idx, *counts, *offsets, *perm, *slot;
+  float *gate, *gap;
+};
+
+int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const float* bias,
+              const RoutePtrs& r, void* ws, const Layout& L, int bm_a, int bm_b,
+              hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, H = c.hidden;
+  float* P = at<float>(ws, L.P);
+  MOE_TRY(timed(K_ROUTER, st, [&] {
+    return moe::launch_router(x, c.act_dtype == MOE_BF16, wr, P, T, H, E, st);
+  }));
+  MOE_TRY(timed(K_SELECT, st, [&] {
+    return moe::launch_select(P, moe::router_ksplit(H), bias, T, E, c.n_groups, c.topk_groups, K,
+                              c.group_topn, r.idx, r.gate, r.gap, st);
+  }));
+  MOE_TRY(timed(K_PERMUTE, st, [&] {
+    return moe::launch_permute(r.idx, T, K, E, c.n_shared, at<uint64_t>(ws, L.masks),
+                               at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base), r.counts,
+                               r.offsets, r.perm, r.slot, bm_a, at<int32_t>(ws, L.mt_a), bm_b,
+                               at<int32_t>(ws, L.mt_b), st);
+  }));
+  return MOE_OK;
+}
+
+RoutePtrs route_ptrs(const moe_routing* out, void* ws, const Layout& L) {
+  RoutePtrs r;
+  if (out != nullptr) {
+    r = RoutePtrs{out->topk_idx, out->counts, out->offsets, out->perm, out->slot, out->topk_gate,
+                  out->tie_gap};
+  } else {
+    r = RoutePtrs{at<int32_t>(ws, L.idx), at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                  at<int32_t>(ws, L.perm), at<int32_t>(ws, L.slot), at<float>(ws, L.gate),
+                  at<float>(ws, L.gap)};
+  }
+  return r;
+}
+
+int check_routing(const moe_routing* out) {
+  if (out == nullptr) return MOE_ERR_NULL;
+  if (!out->topk_idx || !out->topk_gate || !out->counts || !out->offsets || !out->perm || !out->slot)
+    return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+template <typename TE>
+int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, const TE* residual,
+                TE* y, const RoutePtrs& r, void* ws, const Layout& L, int bm, hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
+  const int TK = T * K;
+  const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
+  TE* hst = at<TE>(ws, L.hst);
+  TE* yst = at<TE>(ws, L.yst);
+  moe::GemmArgs<TE> g1{x, static_cast<const TE*>(w->w_gate), static_cast<const TE*>(w->w_up), hst,
+                       r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_a), E, E + S, T, TK, I, H};
+  MOE_TRY(timed(K_GATEUP, st, [&] { return moe::launch_gemm<TE>(g1, true, max_mt, st); }));
+  moe::GemmArgs<TE> g2{hst, static_cast<const TE*>(w->w_down), nullptr, yst, r.perm, r.counts,
+                       r.offsets, at<int32_t>(ws, L.mt_b), E, E + S, T, TK, H, I};
+  MOE_TRY(timed(K_DOWN, st, [&] { return moe::launch_gemm<TE>(g2, false, max_mt, st); }));
+  MOE_TRY(timed(K_COMBINE, st, [&] {
+    return moe::launch_combine<TE>(yst, r.slot, r.gate, residual, y, T, K, H, TK, S, st);
+  }));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return 100; }
+
+int moe_profile_enable(int on) {
+  g_prof.on = on != 0;
+  return MOE_OK;
+}
+
+int moe_profile_read(double* total_ms, int32_t* launches, int n_slots) {
+  for (auto& r : g_prof.recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return MOE_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return MOE_ERR_HIP;
+    g_prof.ms[r.slot] += ms;
+    g_prof.n[r.slot] += 1;
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  for (int i = 0; i < K_NSLOTS && i < n_slots; ++i) {
+    if (total_ms) total_ms[i] = g_prof.ms[i];
+    if (launches) launches[i] = g_prof.n[i];
+  }
+  if (total_ms != nullptr || launches != nullptr) {
+    for (int i = 0; i < K_NSLOTS; ++i) {
+      g_prof.ms[i] = 0.0;
+      g_prof.n[i] = 0;
+    }
+  }
+  return K_NSLOTS;
+}
+
+const char* moe_profile_kernel_name(int slot) {
+  return (slot >= 0 && slot < K_NSLOTS) ? kSlotNames[slot] : "unknown";
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case MOE_ERR_DTYPE: return "unsupported dtype combination";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case MOE_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_cfg* cfg, int64_t T) {
+  if (validate_cfg(cfg) != MOE_OK || validate_T(cfg, T) != MOE_OK) return 0;
+  return make_layout(*cfg, T).total;
+}
+
+int moe_route(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+              const float* bias, const moe_routing* out, void* ws, size_t ws_bytes,
+              void* stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if ((rc = check_routing(out)) != MOE_OK) return rc;
+  if (x == nullptr || w_router == nullptr || bias == nullptr) return MOE_ERR_NULL;
+  if (T == 0) return MOE_OK;
+  const Layout L = make_layout(*cfg, T);
+  if (ws == nullptr || ws_bytes < L.route_total) return MOE_ERR_WORKSPACE;
+  if ((rc = check_device()) != MOE_OK) return rc;
+  const int bm = moe::gemm_tile_m();
+  return run_route(*cfg, int(T), x, w_router, bias, route_ptrs(out, ws, L), ws, L, bm, bm,
+                   static_cast<hipStream_t>(stream));
+}
+
+int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+                const float* bias, const moe_experts* w, const void* residual, void* y,
+                const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if (out != nullptr && (rc = check_routing(out)) != MOE_OK) return rc;
+  if (x == nullptr || w_router == nullptr || bias == nullptr || w == nullptr || y == nullptr)
+    return MOE_ERR_NULL;
+  if (w->w_gate == nullptr || w->w_up == nullptr || w->w_down == nullptr) return MOE_ERR_NULL;
+  if (T == 0) return MOE_OK;
+  const Layout L = make_layout(*cfg, T);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if ((rc = check_device()) != MOE_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int bm = moe::gemm_tile_m();
+  const RoutePtrs r = route_ptrs(out, ws, L);
+  rc = run_route(*cfg, int(T), x, w_router, bias, r, ws, L, bm, bm, st);
+  if (rc != MOE_OK) return rc;
+  if (cfg->act_dtype == MOE_BF16)
+    return run_experts<bf16_t>(*cfg, int(T), static_cast<const bf16_t*>(x), w,
+                               static_cast<const bf16_t*>(residual), static_cast<bf16_t*>(y), r,
+                               ws, L, bm, st);
+  return run_experts<float>(*cfg, int(T), static_cast<const float*>(x), w,
+                            static_cast<const float*>(residual), static_cast<float*>(y), r, ws, L,
+                            bm, st);
+}
+
+int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float* bias,
+                    float gamma, void* stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if (counts == nullptr || bias == nullptr) return MOE_ERR_NULL;
+  if (T == 0) return MOE_OK;
+  if ((rc = check_device()) != MOE_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_TRY(timed(K_BIAS, st, [&] {
+    return moe::launch_bias_update(counts, bias, cfg->n_experts, (long long)T * cfg->topk, gamma,
+                                   st);
+  }));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,434 @@
+// Routing kernels for gfx950: router logits, node-limited top-K selection with
+// the loss-free bias and gates, expert histogram / prefix sum / stable
+// permutation, and the bias step.
+//
+// Method: "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token", §1.3 (Eq 13, 15)
+// and §1.4 (Eq 16).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ============================================================================
+// Router logits, split over K: P[ks][t][e] = sum_{h in chunk ks} x[t][h] W_r[h][e]
+//
+// fp32 MFMA 16x16x4.  Block: 256 threads (4 waves), tile 32 tokens x 256
+// experts; wave w owns experts [64w, 64w+64) as 2 x 4 MFMA tiles.  Each block
+// walks its K chunk in steps of 32 through LDS.  Partial sums of the chunks are
+// added in a fixed order by the select kernel, so the logits are deterministic
+// and each float32 accumulation chain is short.
+// ============================================================================
+
+namespace {
+constexpr int RB_M = 32, RB_N = 256, RB_K = 32;
+constexpr int RA_STRIDE = RB_K + 2;    // A_s row stride (floats): 2 mod 32 banks
+constexpr int RB_STRIDE = RB_N + 16;   // B_s row stride (floats): 16 mod 32 banks
+}  // namespace
+
+template <typename TA>
+__global__ __launch_bounds__(256) void router_logits_kernel(const TA* __restrict__ x,
+                                                            const float* __restrict__ wr,
+                                                            float* __restrict__ P, int T, int H,
+                                                            int E, int kchunk) {
+  __shared__ float A_s[RB_M * RA_STRIDE];
+  __shared__ float B_s[RB_K * RB_STRIDE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RB_M;
+  const int e0 = blockIdx.y * RB_N;
+  const int ks = blockIdx.z;
+  const int k_begin = ks * kchunk;
+  const int k_end = min(H, k_begin + kchunk);
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += RB_K) {
+    // A: 32 x 32 -> 1024 elements, 4 per thread
+    for (int i = tid; i < RB_M * RB_K; i += 256) {
+      int r = i / RB_K, c = i % RB_K;
+      int t = t0 + r, k = k0 + c;
+      float v = (t < T && k < k_end) ? to_f32(x[(size_t)t * H + k]) : 0.f;
+      A_s[r * RA_STRIDE + c] = v;
+    }
+    // B: 32 x 256 floats, float4 loads
+    for (int i = tid; i < RB_K * RB_N / 4; i += 256) {
+      int r = i / (RB_N / 4), c4 = (i % (RB_N / 4)) * 4;
+      int k = k0 + r, e = e0 + c4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < k_end) {
+        if ((E & 3) == 0 && e + 3 < E) {
+          v = *reinterpret_cast<const float4*>(wr + (size_t)k * E + e);
+        } else {
+          float tmp[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int q = 0; q < 4; ++q)
+            if (e + q < E) tmp[q] = wr[(size_t)k * E + e + q];
+          v = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        }
+      }
+      float* dst = &B_s[r * RB_STRIDE + c4];
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < RB_K; kk += 4) {
+      float a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = A_s[(i * 16 + (lane & 15)) * RA_STRIDE + kk + (lane >> 4)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = B_s[(kk + (lane >> 4)) * RB_STRIDE + wave * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // D layout: lane holds rows 4*(lane/16)+q, column lane%16
+  float* Pk = P + (size_t)ks * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int t = t0 + i * 16 + 4 * (lane >> 4) + q;
+        int e = e0 + wave * 64 + j * 16 + (lane & 15);
+        if (t < T && e < E) Pk[(size_t)t * E + e] = acc[i][j][q];
+      }
+}
+
+
+// ============================================================================
+// Node-limited selection, one wave per token.
+//
+// Lane l holds experts [l*epl, (l+1)*epl).  L = sum of the split-K partials in
+// chunk order; s = sigmoid(L); z = s + b.  Group scores (sum of the group_topn
+// largest z of each contiguous group, added from the largest down) are formed
+// by lanes 0..G-1 from LDS.  topk_groups rounds of a wave arg-max keep the
+// groups, topk rounds pick the experts among the kept groups' experts; one
+// extra round of each measures the near-tie gaps.  Ties go to the lower index.
+// Gates are the chosen s divided by their float32 sum.  Output ids ascend.
+// ============================================================================
+
+constexpr int SEL_WAVES = 4;
+constexpr int SEL_MAX_E = 512;
+
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ P, int ksplit,
+                                                     const float* __restrict__ bias, int T, int E,
+                                                     int G, int topk_groups, int topk,
+                                                     int group_topn, int32_t* __restrict__ idx_out,
+                                                     float* __restrict__ gate_out,
+                                                     float* __restrict__ gap_out) {
+  __shared__ float z_s[SEL_WAVES][SEL_MAX_E];
+  __shared__ float s_s[SEL_WAVES][SEL_MAX_E];
+  __shared__ int sel_s[SEL_WAVES][33];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t_raw = blockIdx.x * SEL_WAVES + wave;
+  const bool valid = t_raw < T;  // no early exit: the block meets at barriers below
+  const int t = valid ? t_raw : T - 1;
+  const int epl = (E + 63) / 64;
+  const int gsz = E / G;
+  float* z = z_s[wave];
+  float* s = s_s[wave];
+
+  for (int j = 0; j < epl; ++j) {
+    int e = lane * epl + j;
+    if (e < E) {
+      float L = 0.f;
+      for (int k = 0; k < ksplit; ++k) L += P[((size_t)k * T + t) * E + e];
+      float sv = sigmoidf(L);
+      s[e] = sv;
+      z[e] = sv + bias[e];
+    }
+  }
+  __syncthreads();
+
+  // group scores: lane g < G scans its group keeping the group_topn largest (descending)
+  float gscore = -INFINITY;
+  int gidx = 0x7fffffff;
+  if (lane < G) {
+    float top[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int i = 0; i < gsz; ++i) {
+      float v = z[lane * gsz + i];
+      // insert into the descending list of length group_topn
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q < group_topn && v > top[q]) {
+          float tmp = top[q];
+          top[q] = v;
+          v = tmp;
+        }
+      }
+    }
+    float acc = top[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q)
+      if (q < group_topn) acc += top[q];
+    gscore = acc;
+    gidx = lane;
+  }
+  // keep topk_groups groups; one more round for the gap
+  uint64_t kept = 0;
+  float glast = 0.f, gnext = -INFINITY;
+  {
+    float v = gscore;
+    int i = gidx;
+    for (int r = 0; r <= topk_groups && r < G; ++r) {
+      float bv = v;
+      int bi = i;
+      wave_argmax(bv, bi);
+      if (r < topk_groups) {
+        kept |= (1ull << bi);
+        glast = bv;
+      } else {
+        gnext = bv;
+      }
+      if (lane == bi) {
+        v = -INFINITY;
+        i = 0x7fffffff;
+      }
+    }
+  }
+  // expert rounds among the kept groups
+  float zl[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int e = lane * epl + j;
+    zl[j] = (j < epl && e < E && ((kept >> (e / gsz)) & 1ull)) ? z[e] : -INFINITY;
+  }
+  float elast = 0.f, enext = -INFINITY;
+  for (int r = 0; r <= topk; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (zl[j] > bv) {  // lanes hold ascending ids: strict '>' keeps the lower id
+        bv = zl[j];
+        bi = lane * epl + j;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (r < topk) {
+      if (lane == 0) sel_s[wave][r] = bi;
+      elast = bv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (lane * epl + j == bi) zl[j] = -INFINITY;
+    } else {
+      enext = bv;
+    }
+  }
+  __syncthreads();
+  // sort the chosen ids ascending and write ids and gates
+  float ssum = 0.f;
+  for (int r = 0; r < topk; ++r) ssum += s[sel_s[wave][r]];
+  if (valid && lane < topk) {
+    int me = sel_s[wave][lane];
+    int rank = 0;
+    for (int r = 0; r < topk; ++r) rank += (sel_s[wave][r] < me) ? 1 : 0;
+    idx_out[(size_t)t * topk + rank] = me;
+    gate_out[(size_t)t * topk + rank] = s[me] / ssum;
+  }
+  if (valid && gap_out != nullptr && lane == 0) {
+    float eg = (enext == -INFINITY) ? INFINITY : (elast - enext);
+    float gg = (topk_groups >= G || gnext == -INFINITY) ? INFINITY : (glast - gnext);
+    gap_out[t] = fminf(eg, gg);
+  }
+}
+
+// ============================================================================
+// Stable permutation by expert (integer work, deterministic).
+//
+// Tokens are cut into chunks of 64.  hist: per chunk, a 64-bit token mask per
+// expert (LDS atomic OR, order-free) and its popcount.  scan (one block): counts,
+// offsets, and each chunk's first row per expert; also the GEMM m-tile starts.
+// scatter: the row of assignment (t,k) is the chunk base of its expert plus the
+// number of earlier tokens of the chunk that chose the same expert.
+// ============================================================================
+
+constexpr int CHUNK = 64;
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                   int E, uint64_t* __restrict__ masks,
+                                                   int32_t* __restrict__ hist) {
+  __shared__ unsigned long long m_s[SEL_MAX_E];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) m_s[e] = 0ull;
+  __syncthreads();
+  const int t0 = c * CHUNK;
+  const int nt = min(CHUNK, T - t0);
+  for (int a = threadIdx.x; a < nt * K; a += blockDim.x) {
+    int tl = a / K;
+    int e = idx[(size_t)(t0 + tl) * K + (a % K)];
+    atomicOr(&m_s[e], 1ull << tl);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    masks[(size_t)c * E + e] = m_s[e];
+    hist[(size_t)c * E + e] = __popcll(m_s[e]);
+  }
+}
+
+// tiles: m-tile starts for two tile heights, over E routed experts then the
+// S shared experts (T rows each).  mt_a/mt_b have E+S+1 entries.
+__global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ hist, int nchunks,
+                                                   int E, int S, int T, int K,
+                                                   int32_t* __restrict__ base,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets, int bm_a,
+                                                   int32_t* __restrict__ mt_a, int bm_b,
+                                                   int32_t* __restrict__ mt_b) {
+  __shared__ int sc[SEL_MAX_E + 2];
+  __shared__ int ta[SEL_MAX_E + 2];
+  __shared__ int tb[SEL_MAX_E + 2];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) cnt += hist[(size_t)c * E + e];
+  if (e < E) {
+    sc[e] = cnt;
+    ta[e] = (cnt + bm_a - 1) / bm_a;
+    tb[e] = (cnt + bm_b - 1) / bm_b;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0, aa = 0, ab = 0;
+    for (int i = 0; i < E; ++i) {
+      int v = sc[i];
+      sc[i] = acc;
+      acc += v;
+      int va = ta[i];
+      ta[i] = aa;
+      aa += va;
+      int vb = tb[i];
+      tb[i] = ab;
+      ab += vb;
+    }
+    sc[E] = acc;
+    for (int sh = 0; sh < S; ++sh) {
+      ta[E + sh] = aa;
+      aa += (T + bm_a - 1) / bm_a;
+      tb[E + sh] = ab;
+      ab += (T + bm_b - 1) / bm_b;
+    }
+    ta[E + S] = aa;
+    tb[E + S] = ab;
+  }
+  __syncthreads();
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = sc[e];
+    int run = sc[e];
+    for (int c = 0; c < nchunks; ++c) {
+      base[(size_t)c * E + e] = run;
+      run += hist[(size_t)c * E + e];
+    }
+  }
+  if (e == 0) offsets[E] = sc[E];
+  for (int i = e; i <= E + S; i += blockDim.x) {
+    mt_a[i] = ta[i];
+    mt_b[i] = tb[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, int T,
+                                                      int K, int E,
+                                                      const uint64_t* __restrict__ masks,
+                                                      const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ slot) {
+  const int c = blockIdx.x;
+  const int t0 = c * CHUNK;
+  const int nt = min(CHUNK, T - t0);
+  for (int a = threadIdx.x; a < nt * K; a += blockDim.x) {
+    int tl = a / K;
+    int t = t0 + tl;
+    int e = idx[(size_t)t * K + (a % K)];
+    uint64_t m = masks[(size_t)c * E + e];
+    uint64_t below = (tl == 0) ? 0ull : (m & ((1ull << tl) - 1ull));
+    int row = base[(size_t)c * E + e] + __popcll(below);
+    slot[(size_t)t * K + (a % K)] = row;
+    perm[row] = t;
+  }
+}
+
+// ============================================================================
+// Loss-free bias step ([V3] §1.4): one thread per expert.
+// ============================================================================
+
+__global__ void bias_update_kernel(const int32_t* __restrict__ counts, float* __restrict__ bias,
+                                   int E, long long TK, float gamma) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  long long load = (long long)counts[e] * E;
+  float b = bias[e];
+  if (load > TK) b = b - gamma;
+  else if (load < TK) b = b + gamma;
+  bias[e] = b;
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+
+// number of K chunks of the router: chunks of at most ~H/8, multiples of 32
+int router_ksplit(int H) {
+  int chunk = ((H + 7) / 8 + RB_K - 1) / RB_K * RB_K;
+  return (H + chunk - 1) / chunk;
+}
+
+hipError_t launch_router(const void* x, bool x_bf16, const float* wr, float* P, int T, int H,
+                         int E, hipStream_t st) {
+  const int ks = router_ksplit(H);
+  const int chunk = ((H + 7) / 8 + RB_K - 1) / RB_K * RB_K;
+  dim3 grid((T + RB_M - 1) / RB_M, (E + RB_N - 1) / RB_N, ks);
+  if (x_bf16)
+    hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(x), wr, P, T, H, E, chunk);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, st,
+                       static_cast<const float*>(x), wr, P, T, H, E, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* P, int ksplit, const float* bias, int T, int E, int G,
+                         int topk_groups, int topk, int group_topn, int32_t* idx, float* gate,
+                         float* gap, hipStream_t st) {
+  dim3 grid((T + SEL_WAVES - 1) / SEL_WAVES);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(64 * SEL_WAVES), 0, st, P, ksplit, bias, T, E, G,
+                     topk_groups, topk, group_topn, idx, gate, gap);
+  return hipGetLastError();
+}
+
+int perm_chunks(int T) { return (T + CHUNK - 1) / CHUNK; }
+
+hipError_t launch_permute(const int32_t* idx, int T, int K, int E, int S, uint64_t* masks,
+                          int32_t* hist, int32_t* base, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* slot, int bm_a, int32_t* mt_a, int bm_b,
+                          int32_t* mt_b, hipStream_t st) {
+  const int nc = perm_chunks(T);
+  hipLaunchKernelGGL(hist_kernel, dim3(nc), dim3(256), 0, st, idx, T, K, E, masks, hist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(512), 0, st, hist, nc, E, S, T, K, base, counts,
+                     offsets, bm_a, mt_a, bm_b, mt_b);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), 0, st, idx, T, K, E, masks, base, perm,
+                     slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, long long TK,
+                              float gamma, hipStream_t st) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((E + 255) / 256), dim3(256), 0, st, counts, bias, E,
+                     TK, gamma);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,132 @@
+"""C ABI contract on the host: the library loads, exports every entry point that
+include/moe.h declares, and rejects bad arguments with status codes before any
+GPU work.  No compute call is made here (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_moe_layer_group_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.lib_path()),
+                                reason="library not built (python -m sparse_moe_layer_group_amd.build)")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared() == sorted(moe.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.lib_path()], capture_output=True, text=True)
+    exported = set(l.split()[-1] for l in out.stdout.splitlines() if " T " in l)
+    assert set(_declared()) <= exported
+
+
+def test_status_strings_and_version():
+    assert moe.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5, -6):
+        assert moe.status_string(s) != "unknown status"
+    assert moe.abi_version() == 100
+
+
+def _v3(**kw):
+    base = dict(hidden=7168, inter=2048, n_experts=256, n_groups=8, topk_groups=4, topk=8,
+                group_topn=2, n_shared=1, act_dtype=moe.BF16, w_dtype=moe.BF16)
+    base.update(kw)
+    return moe.make_cfg(**base)
+
+
+def test_workspace_bytes_is_positive_and_grows_with_T():
+    c = _v3()
+    a, b = moe.workspace_bytes(c, 256), moe.workspace_bytes(c, 8192)
+    assert 0 < a < b
+    # staging for T*(K+1) rows of H and I, bf16, dominates
+    assert b >= 8192 * 9 * (7168 + 2048) * 2
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_groups=7),                     # E % G != 0
+    dict(topk=33),                        # K > 32
+    dict(topk_groups=9),                  # more groups kept than exist
+    dict(group_topn=5),                   # > 4
+    dict(topk=8, topk_groups=1, n_experts=16, n_groups=8),   # K > experts in kept groups
+    dict(hidden=7100),                    # not a multiple of 128
+    dict(n_shared=2),
+    dict(n_experts=1024, n_groups=8),
+])
+def test_bad_shapes_are_rejected(kw):
+    c = _v3(**kw)
+    assert moe.workspace_bytes(c, 16) == 0
+    L = moe.lib()
+    r = moe._Routing(*([1] * 7))
+    rc = L.moe_route(ctypes.byref(c), 16, ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                     ctypes.byref(r), ctypes.c_void_p(1), 1 << 40, None)
+    assert rc == -2
+
+
+def test_bad_dtypes_are_rejected():
+    L = moe.lib()
+    for act, w in ((moe.F32, moe.BF16), (moe.BF16, moe.F32), (moe.E4M3, moe.E4M3)):
+        c = _v3(act_dtype=act, w_dtype=w)
+        r = moe._Routing(*([1] * 7))
+        rc = L.moe_route(ctypes.byref(c), 16, ctypes.c_void_p(1), ctypes.c_void_p(1),
+                         ctypes.c_void_p(1), ctypes.byref(r), ctypes.c_void_p(1), 1 << 40, None)
+        assert rc == -3
+
+
+def test_null_pointers_and_small_workspace_are_rejected():
+    L = moe.lib()
+    c = _v3()
+    r = moe._Routing(*([1] * 7))
+    one = ctypes.c_void_p(1)
+    assert L.moe_route(None, 16, one, one, one, ctypes.byref(r), one, 1 << 40, None) == -1
+    assert L.moe_route(ctypes.byref(c), 16, None, one, one, ctypes.byref(r), one, 1 << 40, None) == -1
+    assert L.moe_route(ctypes.byref(c), 16, one, one, None, ctypes.byref(r), one, 1 << 40, None) == -1
+    assert L.moe_route(ctypes.byref(c), 16, one, one, one, None, one, 1 << 40, None) == -1
+    r2 = moe._Routing(1, 1, None, 1, 1, 1, None)
+    assert L.moe_route(ctypes.byref(c), 16, one, one, one, ctypes.byref(r2), one, 1 << 40, None) == -1
+    assert L.moe_route(ctypes.byref(c), 16, one, one, one, ctypes.byref(r), None, 1 << 40, None) == -4
+    assert L.moe_route(ctypes.byref(c), 16, one, one, one, ctypes.byref(r), one, 100, None) == -4
+    ex = moe._Experts(1, 1, None, None, None, None)
+    assert L.moe_forward(ctypes.byref(c), 16, one, one, one, ctypes.byref(ex), None, one, None, one,
+                         1 << 40, None) == -1
+    assert L.moe_bias_update(ctypes.byref(c), 16, None, one, ctypes.c_float(1e-3), None) == -1
+    assert L.moe_route(ctypes.byref(c), -1, one, one, one, ctypes.byref(r), one, 1 << 40, None) == -2
+    assert L.moe_route(ctypes.byref(c), 1 << 28, one, one, one, ctypes.byref(r), one, 1 << 62,
+                       None) == -2
+
+
+def test_zero_tokens_is_a_no_op():
+    L = moe.lib()
+    c = _v3()
+    r = moe._Routing(*([1] * 7))
+    one = ctypes.c_void_p(1)
+    assert L.moe_route(ctypes.byref(c), 0, one, one, one, ctypes.byref(r), None, 0, None) == 0
+    ex = moe._Experts(1, 1, 1, None, None, None)
+    assert L.moe_forward(ctypes.byref(c), 0, one, one, one, ctypes.byref(ex), None, one, None, None,
+                         0, None) == 0
+    assert L.moe_bias_update(ctypes.byref(c), 0, one, one, ctypes.c_float(1e-3), None) == 0
+
+
+def test_binding_has_no_cpu_fallback():
+    # the package source must not import the oracle or compute on the host
+    pkg = os.path.join(ROOT, "sparse_moe_layer_group_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("the oracle", ""), fn
+            assert "synthetic" not in src, fn

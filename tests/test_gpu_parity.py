@@ -1,0 +1,153 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: selections, counts, permutation and bias updates bit-exact (near-ties
+with a gap < 1e-6 are flagged and only checked for validity); gates within
+1e-6; layer output within a max row-relative error of 1e-5 (fp32), 2e-2
+(bf16) or 6e-2 (fp8 E4M3).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_moe_layer_group_amd as moe
+import synthetic as S
+from tests.conftest import gpu_available
+from tests.gpu_common import (DEV, OUT_TOL, GpuInputs, check_routing, cpu_expert_source,
+                              oracle_route, row_errors, say)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _oracle_forward(c, tokens=None, x_cpu=None, b=None):
+    x_cpu = S.gen_x(c, device="cpu") if x_cpu is None else x_cpu
+    b = S.gen_bias(c, "cpu").numpy() if b is None else b
+    return O.forward(O.lift(x_cpu), O.lift(S.gen_router(c, "cpu")), b, cpu_expert_source(c),
+                     n_groups=c.n_groups, topk_groups=c.topk_groups, topk=c.topk,
+                     group_topn=c.group_topn, n_shared=c.n_shared, tokens=tokens)
+
+
+# --------------------------------------------------------------------------- inputs
+
+
+def test_generator_is_identical_on_gpu_and_cpu():
+    for name in ("tiny", "decode", "fp8"):
+        c = S.get_config(name)
+        assert torch.equal(S.gen_x(c, device=DEV, rows=slice(5, 37)).cpu(),
+                           S.gen_x(c, device="cpu", rows=slice(5, 37)))
+        assert torch.equal(S.gen_router(c, DEV).cpu(), S.gen_router(c, "cpu"))
+        for e in (0, c.n_experts):
+            g, h = S.gen_expert(c, e, DEV), S.gen_expert(c, e, "cpu")
+            for k in g:
+                assert torch.equal(g[k].cpu(), h[k]), (name, e, k)
+    say("generator: GPU and CPU streams identical")
+
+
+# --------------------------------------------------------------------------- full-output parity
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("tiny", 1), ("tiny", 67), ("mid", 300),
+                                    ("mid", 1), ("mid", 65), ("mid", 129)])
+def test_forward_full_parity(name, T):
+    c = S.get_config(name, T=T)
+    say(f"forward parity: {name} T={T}")
+    gi = GpuInputs(c)
+    y, out = gi.run_forward()
+    ref = _oracle_forward(c)
+    check_routing(c, out, ref.routing, f"{name} T={T}")
+    err = row_errors(y.float().cpu().numpy(), ref.y)
+    say(f"{name} T={T}: max row rel err {err.max():.3e} (median {np.median(err):.3e})")
+    assert err.max() <= OUT_TOL[c.act_dtype if c.w_dtype != "e4m3" else "e4m3"]
+
+
+def test_forward_with_residual():
+    c = S.get_config("mid", T=100)
+    gi = GpuInputs(c)
+    y0, _ = gi.run_forward()
+    y1, _ = gi.run_forward(residual=gi.x)
+    ref = _oracle_forward(c)
+    ref_res = ref.y + O.lift(gi.x.cpu())
+    assert row_errors(y1.float().cpu().numpy(), ref_res).max() <= 2e-2
+    assert not torch.equal(y0, y1)
+
+
+def test_forward_is_deterministic():
+    c = S.get_config("mid", T=300)
+    gi = GpuInputs(c)
+    y0, o0 = gi.run_forward()
+    y1, o1 = gi.run_forward()
+    assert torch.equal(y0, y1)
+    for k in o0:
+        assert torch.equal(o0[k], o1[k]), k
+
+
+def test_zero_tokens():
+    c = S.get_config("mid", T=4)
+    gi = GpuInputs(c)
+    y = torch.full((0, c.hidden), 7.0, dtype=torch.bfloat16, device=DEV)
+    ws = moe.alloc_workspace(gi.cfg, 0, DEV)
+    moe.forward(gi.cfg, gi.x[:0], gi.wr, gi.b, gi.ex, y, ws)
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- V3 shapes
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_v3_routing_and_sampled_output(name):
+    c = S.get_config(name)
+    say(f"V3 {name}: generating inputs on the GPU (T={c.T})")
+    gi = GpuInputs(c)
+    y, out = gi.run_forward()
+    x_cpu = S.gen_x(c, device="cpu")
+    b = S.gen_bias(c, "cpu").numpy()
+    L, s, r, p = oracle_route(c, x_cpu, b)
+    check_routing(c, out, r, f"V3 {name}")
+    # output on sampled tokens, including ones routed to the busiest expert
+    busiest = int(np.argmax(p.counts))
+    tok_busy = int(p.perm[p.offsets[busiest]])
+    tokens = sorted(set([0, 1, c.T // 2, c.T - 1, tok_busy]))
+    tokens = [t for t in tokens if not r.flagged[t]]
+    ref = _oracle_forward(c, tokens=tokens, x_cpu=x_cpu, b=b)
+    err = row_errors(y[tokens].float().cpu().numpy(), ref.y)
+    say(f"V3 {name}: sampled tokens {tokens}: row rel err {np.round(err, 5).tolist()}")
+    assert err.max() <= OUT_TOL["bf16"]
+    del gi, y, out
+    _free()
+
+
+# --------------------------------------------------------------------------- bias step
+
+
+def test_bias_update_bit_exact_and_skew_steps():
+    c = S.get_config("skew", T=1024)
+    cfg = moe.cfg_from(c)
+    wr = S.gen_router(c, DEV)
+    b = torch.zeros(c.n_experts, dtype=torch.float32, device=DEV)
+    ws = moe.alloc_workspace(cfg, c.T, DEV)
+    b_ref = np.zeros(c.n_experts, np.float32)
+    ratios = []
+    for step in range(12):
+        x = S.gen_x(c, step=step, device=DEV)
+        out = moe.alloc_routing(cfg, c.T, DEV)
+        moe.route(cfg, x, wr, b, out, ws)
+        counts = out["counts"]
+        moe.bias_update(cfg, c.T, counts, b, c.gamma)
+        torch.cuda.synchronize()
+        # the GPU's counts come from its selection; check it against the oracle
+        L, s, r, p = oracle_route(c, S.gen_x(c, step=step, device="cpu"), b_ref)
+        check_routing(c, out, r, f"skew step {step}")
+        b_ref = O.bias_update(b_ref, out["counts"].cpu().numpy(), c.T, c.topk, c.gamma)
+        assert np.array_equal(b.cpu().numpy().view(np.uint32), b_ref.view(np.uint32)), step
+        ratios.append(O.load_ratio(out["counts"].cpu().numpy()))
+    say(f"skew: max/mean load per step {np.round(ratios, 2).tolist()}")
+    assert ratios[-1] < ratios[0]
