@@ -30,7 +30,8 @@
  *    argument validation and launch errors; a fault while the kernels run is
  *    reported by the caller's next synchronisation.
  *  - On a validation error nothing is launched and no output is written.
- *  - T == 0 returns MOE_OK and launches nothing.
+ *  - T == 0 returns MOE_OK once the cfg is valid, without reading any
+ *    pointer (they may be NULL) and without launching.
  *  - Results are deterministic: the same inputs give bitwise identical outputs
  *    (no floating-point atomics; integer atomics only where the result does
  *    not depend on their order).

@@ -273,9 +273,9 @@ int moe_route(const moe_cfg* cfg, int64_t T, const void* x, const float* w_route
   int rc = validate_cfg(cfg);
   if (rc != MOE_OK) return rc;
   if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
   if ((rc = check_routing(out)) != MOE_OK) return rc;
   if (x == nullptr || w_router == nullptr || bias == nullptr) return MOE_ERR_NULL;
-  if (T == 0) return MOE_OK;
   const Layout L = make_layout(*cfg, T);
   if (ws == nullptr || ws_bytes < L.route_total) return MOE_ERR_WORKSPACE;
   if ((rc = check_device()) != MOE_OK) return rc;
@@ -290,11 +290,11 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   int rc = validate_cfg(cfg);
   if (rc != MOE_OK) return rc;
   if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
   if (out != nullptr && (rc = check_routing(out)) != MOE_OK) return rc;
   if (x == nullptr || w_router == nullptr || bias == nullptr || w == nullptr || y == nullptr)
     return MOE_ERR_NULL;
   if (w->w_gate == nullptr || w->w_up == nullptr || w->w_down == nullptr) return MOE_ERR_NULL;
-  if (T == 0) return MOE_OK;
   const Layout L = make_layout(*cfg, T);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if ((rc = check_device()) != MOE_OK) return rc;
@@ -317,8 +317,8 @@ int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float*
   int rc = validate_cfg(cfg);
   if (rc != MOE_OK) return rc;
   if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
-  if (counts == nullptr || bias == nullptr) return MOE_ERR_NULL;
   if (T == 0) return MOE_OK;
+  if (counts == nullptr || bias == nullptr) return MOE_ERR_NULL;
   if ((rc = check_device()) != MOE_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   MOE_TRY(timed(K_BIAS, st, [&] {

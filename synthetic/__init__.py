@@ -290,14 +290,18 @@ def gen_bias(cfg: MoEConfig, device="cpu") -> torch.Tensor:
 def _e4m3_blocks(master: torch.Tensor):
     """Offline weight encoding: one float32 scale per 128x128 block, codes e4m3fn.
 
-    scale = amax / 448 (1 if the block is all zero); code = RNE(v / scale).
+    scale = fl32(amax / 448) (1 if the block is all zero); code = RNE(fl32(v / scale)).
+    Divisions are float64 tensor-by-tensor divisions (torch divides by a scalar
+    on the GPU through a reciprocal), so CPU and GPU give identical encodings.
     Returns (uint8 codes with the master's shape, scales [rows/128][cols/128]).
     """
     R, C = master.shape
     blk = master.view(R // 128, 128, C // 128, 128)
-    amax = blk.abs().amax(dim=(1, 3))
-    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-    q = (blk / scale[:, None, :, None]).to(torch.float8_e4m3fn)
+    amax = blk.abs().amax(dim=(1, 3)).to(torch.float64)
+    d448 = torch.full_like(amax, 448.0)
+    scale = torch.where(amax > 0, amax / d448, torch.ones_like(amax)).to(torch.float32)
+    ratio = (blk.to(torch.float64) / scale.to(torch.float64)[:, None, :, None]).to(torch.float32)
+    q = ratio.to(torch.float8_e4m3fn)
     return q.view(torch.uint8).view(R, C).contiguous(), scale.contiguous()
 
 

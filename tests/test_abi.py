@@ -120,6 +120,10 @@ def test_zero_tokens_is_a_no_op():
     assert L.moe_forward(ctypes.byref(c), 0, one, one, one, ctypes.byref(ex), None, one, None, None,
                          0, None) == 0
     assert L.moe_bias_update(ctypes.byref(c), 0, one, one, ctypes.c_float(1e-3), None) == 0
+    # with no tokens nothing is read: NULL pointers are accepted
+    assert L.moe_forward(ctypes.byref(c), 0, None, None, None, None, None, None, None, None, 0,
+                         None) == 0
+    assert L.moe_route(ctypes.byref(c), 0, None, None, None, None, None, 0, None) == 0
 
 
 def test_binding_has_no_cpu_fallback():
