@@ -9,6 +9,8 @@
 // TK + s*T .. TK + (s+1)*T - 1 (tokens in order).  A launch covers every
 // (m-tile, n-tile) of every expert; m-tiles are numbered by the prefix table
 // mt_start[0..E+S] built on the device, so no host synchronisation is needed.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -94,17 +96,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs<TE> g) {
   __shared__ __attribute__((aligned(16))) TE B_s[NB * STRIDE];
   __shared__ int tok_s[BM];
 
-  const int n_mt = g.mt_start[g.n_exp];
-  const int mt = blockIdx.y;
-  if (mt >= n_mt) return;  // uniform for the block, before any barrier
+  const int n_nt = g.N / BN;
+  const int n_tasks = g.mt_start[g.n_exp] * n_nt;
+  const int K = g.K;
+  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {  // uniform per block
+  const int mt = task / n_nt;
   const int e = find_expert(g.mt_start, g.n_exp, mt);
   const bool shared = e >= g.E;
   const int cnt = shared ? g.T : g.counts[e];
   const int row_base = shared ? g.TK + (e - g.E) * g.T : g.offsets[e];
   const int m0 = (mt - g.mt_start[e]) * BM;
   const int rows = min(BM, cnt - m0);
-  const int n0 = blockIdx.x * BN;
-  const int K = g.K;
+  const int n0 = (task - mt * n_nt) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -183,6 +186,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs<TE> g) {
           g.out[(size_t)(row_base + m0 + r) * g.N + n] = from_f32<TE>(v);
         }
       }
+  __syncthreads();  // tok_s is rewritten by the next task
+  }
 }
 
 // ============================================================================
@@ -244,16 +249,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE* __restrict__ Y,
 // ============================================================================
 
 template <typename TE>
-hipError_t launch_gemm(const GemmArgs<TE>& g, bool gated, int max_mtiles, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs<TE>& g, bool gated, int max_mtiles, int max_blocks,
+                       hipStream_t st) {
   constexpr int BM = 64, BN = 64, BK = 64;
-  dim3 grid(g.N / BN, max_mtiles), block(256);
+  const long long tasks = (long long)max_mtiles * (g.N / BN);
+  dim3 grid((unsigned)std::min<long long>(tasks, max_blocks)), block(256);
   if (gated) hipLaunchKernelGGL((grouped_gemm_kernel<TE, true, BM, BN, BK>), grid, block, 0, st, g);
   else hipLaunchKernelGGL((grouped_gemm_kernel<TE, false, BM, BN, BK>), grid, block, 0, st, g);
   return hipGetLastError();
 }
 
-template hipError_t launch_gemm<bf16_t>(const GemmArgs<bf16_t>&, bool, int, hipStream_t);
-template hipError_t launch_gemm<float>(const GemmArgs<float>&, bool, int, hipStream_t);
+template hipError_t launch_gemm<bf16_t>(const GemmArgs<bf16_t>&, bool, int, int, hipStream_t);
+template hipError_t launch_gemm<float>(const GemmArgs<float>&, bool, int, int, hipStream_t);
 
 int gemm_tile_m() { return 64; }
 

@@ -10,16 +10,17 @@ typedef uint16_t bf16_t;
 
 // ---- routing (route_kernels.hip)
 int router_ksplit(int H);
-hipError_t launch_router(const void* x, bool x_bf16, const float* wr, float* P, int T, int H,
-                         int E, hipStream_t st);
+size_t router_split_bytes(int H, int E);
+hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt3, float* P,
+                         int T, int H, int E, hipStream_t st);
 hipError_t launch_select(const float* P, int ksplit, const float* bias, int T, int E, int G,
                          int topk_groups, int topk, int group_topn, int32_t* idx, float* gate,
                          float* gap, hipStream_t st);
 int perm_chunks(int T);
 hipError_t launch_permute(const int32_t* idx, int T, int K, int E, int S, uint64_t* masks,
                           int32_t* hist, int32_t* base, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* slot, int bm_a, int32_t* mt_a, int bm_b,
-                          int32_t* mt_b, hipStream_t st);
+                          int32_t* perm, int32_t* slot, int stream_max, int32_t* chunk_start,
+                          int bm, int32_t* mt_start, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, long long TK,
                               float gamma, hipStream_t st);
 
@@ -36,9 +37,24 @@ template <typename TE> struct GemmArgs {
   int E, n_exp, T, TK, N, K;
 };
 
+// weight-streaming GEMM (stream_gemm.hip), bf16 only
+struct StreamArgs {
+  const bf16_t* a;            // GATED: x [T][K]; else staged H [rows][K]
+  const bf16_t* w0;           // W_gate or W_down [E+S][N][K]
+  const bf16_t* w1;           // W_up (GATED)
+  bf16_t* out;                // staged rows [rows][N]
+  const int32_t* perm;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* chunk_start; // [E+S+1] prefix of 16-row chunks of streamed experts
+  int E, n_exp, T, TK, N, K;
+};
+hipError_t launch_stream_gemm(const StreamArgs& g, bool gated, int n_blocks, hipStream_t st);
+
 int gemm_tile_m();
 template <typename TE>
-hipError_t launch_gemm(const GemmArgs<TE>& g, bool gated, int max_mtiles, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs<TE>& g, bool gated, int max_mtiles, int max_blocks,
+                       hipStream_t st);
 template <typename TE>
 hipError_t launch_combine(const TE* Y, const int32_t* slot, const float* gate, const TE* residual,
                           TE* y, int T, int K, int H, int TK, int S, hipStream_t st);

@@ -4,6 +4,7 @@
 // arguments and enqueues them on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <vector>
@@ -16,7 +17,8 @@ namespace {
 using moe::bf16_t;
 
 struct Layout {
-  size_t P, idx, gate, counts, offsets, perm, slot, gap, masks, hist, base, mt_a, mt_b;
+  size_t wt3, P, idx, gate, counts, offsets, perm, slot, gap, masks, hist, base, chunk_start,
+      mt_start;
   size_t hst, yst;
   size_t route_total, total;
 };
@@ -36,6 +38,7 @@ Layout make_layout(const moe_cfg& c, int64_t T) {
   const size_t E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
   const size_t TK = size_t(T) * K;
   const size_t nc = size_t(moe::perm_chunks(int(T)));
+  L.wt3 = take(c.act_dtype == MOE_BF16 ? moe::router_split_bytes(c.hidden, c.n_experts) : 0);
   L.P = take(size_t(moe::router_ksplit(c.hidden)) * T * E * 4);
   L.idx = take(TK * 4);
   L.gate = take(TK * 4);
@@ -47,8 +50,8 @@ Layout make_layout(const moe_cfg& c, int64_t T) {
   L.masks = take(nc * E * 8);
   L.hist = take(nc * E * 4);
   L.base = take(nc * E * 4);
-  L.mt_a = take((E + S + 1) * 4);
-  L.mt_b = take((E + S + 1) * 4);
+  L.chunk_start = take((E + S + 1) * 4);
+  L.mt_start = take((E + S + 1) * 4);
   L.route_total = off;
   const size_t rows = TK + S * size_t(T);
   const size_t es = elem_bytes(c.act_dtype);
@@ -149,13 +152,22 @@ struct RoutePtrs {
   float *gate, *gap;
 };
 
+// Experts with at most this many rows go to the weight-streaming GEMM; the
+// rest to the tiled GEMM.  When the average expert has <= 32 rows (decode)
+// every expert streams, the shared one included.
+int stream_max_rows(const moe_cfg& c, int T) {
+  if (c.act_dtype != MOE_BF16) return -1;
+  const long long avg32 = (long long)T * c.topk;
+  return (avg32 <= 32LL * c.n_experts) ? 0x7fffffff : 64;
+}
+
 int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const float* bias,
-              const RoutePtrs& r, void* ws, const Layout& L, int bm_a, int bm_b,
-              hipStream_t st) {
+              const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
   const int E = c.n_experts, K = c.topk, H = c.hidden;
   float* P = at<float>(ws, L.P);
   MOE_TRY(timed(K_ROUTER, st, [&] {
-    return moe::launch_router(x, c.act_dtype == MOE_BF16, wr, P, T, H, E, st);
+    return moe::launch_router(x, c.act_dtype == MOE_BF16, wr, at<bf16_t>(ws, L.wt3), P, T, H, E,
+                              st);
   }));
   MOE_TRY(timed(K_SELECT, st, [&] {
     return moe::launch_select(P, moe::router_ksplit(H), bias, T, E, c.n_groups, c.topk_groups, K,
@@ -164,8 +176,9 @@ int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const flo
   MOE_TRY(timed(K_PERMUTE, st, [&] {
     return moe::launch_permute(r.idx, T, K, E, c.n_shared, at<uint64_t>(ws, L.masks),
                                at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base), r.counts,
-                               r.offsets, r.perm, r.slot, bm_a, at<int32_t>(ws, L.mt_a), bm_b,
-                               at<int32_t>(ws, L.mt_b), st);
+                               r.offsets, r.perm, r.slot, stream_max_rows(c, T),
+                               at<int32_t>(ws, L.chunk_start), moe::gemm_tile_m(),
+                               at<int32_t>(ws, L.mt_start), st);
   }));
   return MOE_OK;
 }
@@ -190,20 +203,67 @@ int check_routing(const moe_routing* out) {
   return MOE_OK;
 }
 
+std::atomic<int> g_cu_count[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename TE>
 int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, const TE* residual,
-                TE* y, const RoutePtrs& r, void* ws, const Layout& L, int bm, hipStream_t st) {
+                TE* y, const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
   const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
   const int TK = T * K;
+  const int bm = moe::gemm_tile_m();
   const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
   TE* hst = at<TE>(ws, L.hst);
   TE* yst = at<TE>(ws, L.yst);
+  const int32_t* chunk_start = at<int32_t>(ws, L.chunk_start);
+  const int32_t* mt_start = at<int32_t>(ws, L.mt_start);
+  const int smax = stream_max_rows(c, T);
+  const bool streams = smax >= 0;
+  const bool tiles = smax < T;  // an expert (or the shared one) can have up to T rows
+  // persistent grid of the streaming GEMM: one 4-wave workgroup per CU, fewer
+  // when the largest task count the routing can produce is smaller
+  auto stream_blocks = [&](int n_slices) {
+    const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
+    const long long waves = chunks * n_slices;
+    return int(std::max<long long>(1, std::min<long long>((waves + 3) / 4, (long long)cu_count())));
+  };
   moe::GemmArgs<TE> g1{x, static_cast<const TE*>(w->w_gate), static_cast<const TE*>(w->w_up), hst,
-                       r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_a), E, E + S, T, TK, I, H};
-  MOE_TRY(timed(K_GATEUP, st, [&] { return moe::launch_gemm<TE>(g1, true, max_mt, st); }));
+                       r.perm, r.counts, r.offsets, mt_start, E, E + S, T, TK, I, H};
+  MOE_TRY(timed(K_GATEUP, st, [&] {
+    if (streams) {
+      moe::StreamArgs sa{reinterpret_cast<const bf16_t*>(x),
+                         static_cast<const bf16_t*>(w->w_gate), static_cast<const bf16_t*>(w->w_up),
+                         reinterpret_cast<bf16_t*>(hst), r.perm, r.counts, r.offsets, chunk_start,
+                         E, E + S, T, TK, I, H};
+      hipError_t err = moe::launch_stream_gemm(sa, true, stream_blocks(I / 64), st);
+      if (err != hipSuccess || !tiles) return err;
+    }
+    return moe::launch_gemm<TE>(g1, true, max_mt, 4 * cu_count(), st);
+  }));
   moe::GemmArgs<TE> g2{hst, static_cast<const TE*>(w->w_down), nullptr, yst, r.perm, r.counts,
-                       r.offsets, at<int32_t>(ws, L.mt_b), E, E + S, T, TK, H, I};
-  MOE_TRY(timed(K_DOWN, st, [&] { return moe::launch_gemm<TE>(g2, false, max_mt, st); }));
+                       r.offsets, mt_start, E, E + S, T, TK, H, I};
+  MOE_TRY(timed(K_DOWN, st, [&] {
+    if (streams) {
+      moe::StreamArgs sa{reinterpret_cast<const bf16_t*>(hst),
+                         static_cast<const bf16_t*>(w->w_down), nullptr,
+                         reinterpret_cast<bf16_t*>(yst), r.perm, r.counts, r.offsets, chunk_start,
+                         E, E + S, T, TK, H, I};
+      hipError_t err = moe::launch_stream_gemm(sa, false, stream_blocks(H / 128), st);
+      if (err != hipSuccess || !tiles) return err;
+    }
+    return moe::launch_gemm<TE>(g2, false, max_mt, 4 * cu_count(), st);
+  }));
   MOE_TRY(timed(K_COMBINE, st, [&] {
     return moe::launch_combine<TE>(yst, r.slot, r.gate, residual, y, T, K, H, TK, S, st);
   }));
@@ -279,8 +339,7 @@ int moe_route(const moe_cfg* cfg, int64_t T, const void* x, const float* w_route
   const Layout L = make_layout(*cfg, T);
   if (ws == nullptr || ws_bytes < L.route_total) return MOE_ERR_WORKSPACE;
   if ((rc = check_device()) != MOE_OK) return rc;
-  const int bm = moe::gemm_tile_m();
-  return run_route(*cfg, int(T), x, w_router, bias, route_ptrs(out, ws, L), ws, L, bm, bm,
+  return run_route(*cfg, int(T), x, w_router, bias, route_ptrs(out, ws, L), ws, L,
                    static_cast<hipStream_t>(stream));
 }
 
@@ -299,17 +358,16 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if ((rc = check_device()) != MOE_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int bm = moe::gemm_tile_m();
   const RoutePtrs r = route_ptrs(out, ws, L);
-  rc = run_route(*cfg, int(T), x, w_router, bias, r, ws, L, bm, bm, st);
+  rc = run_route(*cfg, int(T), x, w_router, bias, r, ws, L, st);
   if (rc != MOE_OK) return rc;
   if (cfg->act_dtype == MOE_BF16)
     return run_experts<bf16_t>(*cfg, int(T), static_cast<const bf16_t*>(x), w,
                                static_cast<const bf16_t*>(residual), static_cast<bf16_t*>(y), r,
-                               ws, L, bm, st);
+                               ws, L, st);
   return run_experts<float>(*cfg, int(T), static_cast<const float*>(x), w,
                             static_cast<const float*>(residual), static_cast<float*>(y), r, ws, L,
-                            bm, st);
+                            st);
 }
 
 int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float* bias,

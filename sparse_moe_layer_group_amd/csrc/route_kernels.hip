@@ -104,6 +104,116 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TA* __restrict
 
 
 // ============================================================================
+// Router logits for bfloat16 activations through bf16 MFMAs.
+//
+// Every float32 router weight is the exact sum of three bfloat16 parts
+// (hi = top 8 significant bits, mid = next 8, lo = rest, each a truncation
+// remainder), so x * w = x*hi + x*mid + x*lo exactly for a bfloat16 x and
+// three bf16 MFMAs give the float32 products with float32 accumulation.
+// router_split writes the parts transposed, Wt3[3][E][H], so both MFMA
+// operands are K-contiguous.
+// ============================================================================
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
+                                                           bf16_t* __restrict__ wt3, int H,
+                                                           int E) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, ee = i % 64;
+    const int k = k0 + kk, e = e0 + ee;
+    tile[kk][ee] = (k < H && e < E) ? wr[(size_t)k * E + e] : 0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int ee = i / 64, kk = i % 64;
+    const int k = k0 + kk, e = e0 + ee;
+    if (k >= H || e >= E) continue;
+    const float w = tile[kk][ee];
+    const uint32_t u = __float_as_uint(w);
+    const uint32_t hi = u & 0xffff0000u;
+    const float r1 = w - __uint_as_float(hi);              // exact
+    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(mid);            // exact, fits 8 bits
+    const size_t o = (size_t)e * H + k;
+    wt3[o] = bf16_t(hi >> 16);
+    wt3[(size_t)E * H + o] = bf16_t(mid >> 16);
+    wt3[2 * (size_t)E * H + o] = bf16_t(__float_as_uint(r2) >> 16);
+  }
+}
+
+// P[ks][t][e] for one K chunk: wave tile 32 tokens x 32 experts (2 x 2 MFMA
+// 16x16x32 tiles), block = 4 waves over 128 experts.  Operands are loaded
+// straight from global memory in MFMA order with the 128-wide step K map of
+// the streaming GEMM (lane l owns k = 32*(l/16) .. +31 of each step).
+__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ wt3,
+                                                          float* __restrict__ P, int T, int H,
+                                                          int E, int kchunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 32;
+  const int e0 = blockIdx.y * 128 + wave * 32;
+  const int ks = blockIdx.z;
+  const int kb = ks * kchunk, ke = min(H, kb + kchunk);
+  if (e0 >= E) return;  // whole wave; no barrier in this kernel
+  const int koff = 32 * (lane >> 4);
+  const bf16_t* arow[2];
+  const bf16_t* brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + i * 16 + (lane & 15);
+    arow[i] = (t < T) ? x + (size_t)t * H + koff : nullptr;
+    const int e = e0 + i * 16 + (lane & 15);
+    brow[i] = (e < E) ? wt3 + (size_t)e * H + koff : nullptr;
+  }
+  const size_t part = (size_t)E * H;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = kb; k < ke; k += 128) {
+    u32x4 a[2][4], b[3][2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        a[i][q] = arow[i] ? *reinterpret_cast<const u32x4*>(arow[i] + k + q * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          b[p][j][q] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j] + p * part + k + q * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[i][q]), __builtin_bit_cast(bf16x8, b[p][j][q]),
+                acc[i][j], 0, 0, 0);
+  }
+  float* Pk = P + (size_t)ks * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + i * 16 + 4 * (lane >> 4) + q;
+        const int e = e0 + j * 16 + (lane & 15);
+        if (t < T && e < E) Pk[(size_t)t * E + e] = acc[i][j][q];
+      }
+}
+
+// ============================================================================
 // Node-limited selection, one wave per token.
 //
 // Lane l holds experts [l*epl, (l+1)*epl).  L = sum of the split-K partials in
@@ -274,15 +384,18 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   }
 }
 
-// tiles: m-tile starts for two tile heights, over E routed experts then the
-// S shared experts (T rows each).  mt_a/mt_b have E+S+1 entries.
+// Work tables of the expert GEMMs over E routed experts then S shared experts
+// (T rows each), both with E+S+1 entries:
+//   chunk_start: prefix of ceil(rows/16) over experts with rows <= stream_max
+//                (served by the weight-streaming GEMM);
+//   mt_start:    prefix of ceil(rows/bm) over the other experts (tiled GEMM).
 __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ hist, int nchunks,
                                                    int E, int S, int T, int K,
                                                    int32_t* __restrict__ base,
                                                    int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ offsets, int bm_a,
-                                                   int32_t* __restrict__ mt_a, int bm_b,
-                                                   int32_t* __restrict__ mt_b) {
+                                                   int32_t* __restrict__ offsets, int stream_max,
+                                                   int32_t* __restrict__ chunk_start, int bm,
+                                                   int32_t* __restrict__ mt_start) {
   __shared__ int sc[SEL_MAX_E + 2];
   __shared__ int ta[SEL_MAX_E + 2];
   __shared__ int tb[SEL_MAX_E + 2];
@@ -292,8 +405,9 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ h
     for (int c = 0; c < nchunks; ++c) cnt += hist[(size_t)c * E + e];
   if (e < E) {
     sc[e] = cnt;
-    ta[e] = (cnt + bm_a - 1) / bm_a;
-    tb[e] = (cnt + bm_b - 1) / bm_b;
+    const bool str = cnt <= stream_max;
+    ta[e] = str ? (cnt + 15) / 16 : 0;
+    tb[e] = str ? 0 : (cnt + bm - 1) / bm;
   }
   __syncthreads();
   if (e == 0) {
@@ -310,11 +424,12 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ h
       ab += vb;
     }
     sc[E] = acc;
+    const bool str = T <= stream_max;
     for (int sh = 0; sh < S; ++sh) {
       ta[E + sh] = aa;
-      aa += (T + bm_a - 1) / bm_a;
+      aa += str ? (T + 15) / 16 : 0;
       tb[E + sh] = ab;
-      ab += (T + bm_b - 1) / bm_b;
+      ab += str ? 0 : (T + bm - 1) / bm;
     }
     ta[E + S] = aa;
     tb[E + S] = ab;
@@ -331,8 +446,8 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ h
   }
   if (e == 0) offsets[E] = sc[E];
   for (int i = e; i <= E + S; i += blockDim.x) {
-    mt_a[i] = ta[i];
-    mt_b[i] = tb[i];
+    chunk_start[i] = ta[i];
+    mt_start[i] = tb[i];
   }
 }
 
@@ -376,23 +491,32 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, float* __
 // launchers
 // ============================================================================
 
-// number of K chunks of the router: chunks of at most ~H/8, multiples of 32
+// K chunks of the router: about H/8 each, a multiple of 128 (H % 128 == 0)
+static int router_chunk(int H) { return ((H + 7) / 8 + 127) / 128 * 128; }
+
 int router_ksplit(int H) {
-  int chunk = ((H + 7) / 8 + RB_K - 1) / RB_K * RB_K;
+  const int chunk = router_chunk(H);
   return (H + chunk - 1) / chunk;
 }
 
-hipError_t launch_router(const void* x, bool x_bf16, const float* wr, float* P, int T, int H,
-                         int E, hipStream_t st) {
+size_t router_split_bytes(int H, int E) { return (size_t)3 * H * E * sizeof(bf16_t); }
+
+hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt3, float* P,
+                         int T, int H, int E, hipStream_t st) {
   const int ks = router_ksplit(H);
-  const int chunk = ((H + 7) / 8 + RB_K - 1) / RB_K * RB_K;
-  dim3 grid((T + RB_M - 1) / RB_M, (E + RB_N - 1) / RB_N, ks);
-  if (x_bf16)
-    hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, st,
-                       static_cast<const bf16_t*>(x), wr, P, T, H, E, chunk);
-  else
+  const int chunk = router_chunk(H);
+  if (x_bf16) {
+    hipLaunchKernelGGL(router_split_kernel, dim3((H + 63) / 64, (E + 63) / 64), dim3(256), 0, st,
+                       wr, wt3, H, E);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 31) / 32, (E + 127) / 128, ks), dim3(256), 0,
+                       st, static_cast<const bf16_t*>(x), wt3, P, T, H, E, chunk);
+  } else {
+    dim3 grid((T + RB_M - 1) / RB_M, (E + RB_N - 1) / RB_N, ks);
     hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, st,
                        static_cast<const float*>(x), wr, P, T, H, E, chunk);
+  }
   return hipGetLastError();
 }
 
@@ -409,14 +533,14 @@ int perm_chunks(int T) { return (T + CHUNK - 1) / CHUNK; }
 
 hipError_t launch_permute(const int32_t* idx, int T, int K, int E, int S, uint64_t* masks,
                           int32_t* hist, int32_t* base, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, int32_t* slot, int bm_a, int32_t* mt_a, int bm_b,
-                          int32_t* mt_b, hipStream_t st) {
+                          int32_t* perm, int32_t* slot, int stream_max, int32_t* chunk_start,
+                          int bm, int32_t* mt_start, hipStream_t st) {
   const int nc = perm_chunks(T);
   hipLaunchKernelGGL(hist_kernel, dim3(nc), dim3(256), 0, st, idx, T, K, E, masks, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(512), 0, st, hist, nc, E, S, T, K, base, counts,
-                     offsets, bm_a, mt_a, bm_b, mt_b);
+                     offsets, stream_max, chunk_start, bm, mt_start);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), 0, st, idx, T, K, E, masks, base, perm,

@@ -99,6 +99,9 @@ CONFIGS: Dict[str, MoEConfig] = {
     "mid": MoEConfig(name="mid", seed=5, T=300, hidden=1024, inter=256, n_experts=64,
                      n_groups=8, topk_groups=4, topk=8, group_topn=2, n_shared=1,
                      bias_kind="uniform", bias_range=0.02),
+    "mid_skew": MoEConfig(name="mid_skew", seed=7, T=300, hidden=1024, inter=256, n_experts=64,
+                          n_groups=8, topk_groups=4, topk=8, group_topn=2, n_shared=1,
+                          zipf_s=1.2),
     "mid_fp8": MoEConfig(name="mid_fp8", seed=6, T=300, hidden=1024, inter=256, n_experts=64,
                          n_groups=8, topk_groups=4, topk=8, group_topn=2, n_shared=1,
                          w_dtype="e4m3", outlier_p=1e-3, outlier_mult=50.0),

@@ -56,7 +56,8 @@ def test_generator_is_identical_on_gpu_and_cpu():
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 64), ("tiny", 1), ("tiny", 67), ("mid", 300),
-                                    ("mid", 1), ("mid", 65), ("mid", 129)])
+                                    ("mid", 1), ("mid", 65), ("mid", 129), ("mid_skew", 300),
+                                    ("mid_skew", 1000)])
 def test_forward_full_parity(name, T):
     c = S.get_config(name, T=T)
     say(f"forward parity: {name} T={T}")
