@@ -51,6 +51,22 @@ struct StreamArgs {
 };
 hipError_t launch_stream_gemm(const StreamArgs& g, bool gated, int n_blocks, hipStream_t st);
 
+// LDS-tiled GEMM for experts with many rows (tile_gemm.hip), bf16 only;
+// kTileM-row tiles, gate/up column tiles of 128, down column tiles of 256
+struct TileArgs {
+  const bf16_t* a;
+  const bf16_t* w0;
+  const bf16_t* w1;
+  bf16_t* out;
+  const int32_t* perm;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* mt_start;    // [E+S+1] prefix of kTileM-row tiles of tiled experts
+  int E, n_exp, T, TK, N, K;
+};
+constexpr int kTileM = 320;
+hipError_t launch_tile_gemm(const TileArgs& g, bool gated, int max_mtiles, hipStream_t st);
+
 int gemm_tile_m();
 template <typename TE>
 hipError_t launch_gemm(const GemmArgs<TE>& g, bool gated, int max_mtiles, int max_blocks,

@@ -161,6 +161,12 @@ int stream_max_rows(const moe_cfg& c, int T) {
   return (avg32 <= 32LL * c.n_experts) ? 0x7fffffff : 64;
 }
 
+// bf16 layers use the 256-row LDS-pipelined tiled GEMM; the float32 layer the
+// 64x64 tiled GEMM.
+bool use_big_tiles(const moe_cfg& c) { return c.act_dtype == MOE_BF16; }
+
+int tile_rows(const moe_cfg& c) { return use_big_tiles(c) ? moe::kTileM : moe::gemm_tile_m(); }
+
 int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const float* bias,
               const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
   const int E = c.n_experts, K = c.topk, H = c.hidden;
@@ -177,7 +183,7 @@ int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const flo
     return moe::launch_permute(r.idx, T, K, E, c.n_shared, at<uint64_t>(ws, L.masks),
                                at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base), r.counts,
                                r.offsets, r.perm, r.slot, stream_max_rows(c, T),
-                               at<int32_t>(ws, L.chunk_start), moe::gemm_tile_m(),
+                               at<int32_t>(ws, L.chunk_start), tile_rows(c),
                                at<int32_t>(ws, L.mt_start), st);
   }));
   return MOE_OK;
@@ -222,8 +228,9 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
                 TE* y, const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
   const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
   const int TK = T * K;
-  const int bm = moe::gemm_tile_m();
+  const int bm = tile_rows(c);
   const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
+  const bool big = use_big_tiles(c);
   TE* hst = at<TE>(ws, L.hst);
   TE* yst = at<TE>(ws, L.yst);
   const int32_t* chunk_start = at<int32_t>(ws, L.chunk_start);
@@ -249,6 +256,12 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
       hipError_t err = moe::launch_stream_gemm(sa, true, stream_blocks(I / 64), st);
       if (err != hipSuccess || !tiles) return err;
     }
+    if (big) {
+      moe::TileArgs ta{reinterpret_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w->w_gate),
+                       static_cast<const bf16_t*>(w->w_up), reinterpret_cast<bf16_t*>(hst), r.perm,
+                       r.counts, r.offsets, mt_start, E, E + S, T, TK, I, H};
+      return moe::launch_tile_gemm(ta, true, max_mt, st);
+    }
     return moe::launch_gemm<TE>(g1, true, max_mt, 4 * cu_count(), st);
   }));
   moe::GemmArgs<TE> g2{hst, static_cast<const TE*>(w->w_down), nullptr, yst, r.perm, r.counts,
@@ -261,6 +274,12 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
                          E, E + S, T, TK, H, I};
       hipError_t err = moe::launch_stream_gemm(sa, false, stream_blocks(H / 128), st);
       if (err != hipSuccess || !tiles) return err;
+    }
+    if (big) {
+      moe::TileArgs ta{reinterpret_cast<const bf16_t*>(hst), static_cast<const bf16_t*>(w->w_down),
+                       nullptr, reinterpret_cast<bf16_t*>(yst), r.perm, r.counts, r.offsets,
+                       mt_start, E, E + S, T, TK, H, I};
+      return moe::launch_tile_gemm(ta, false, max_mt, st);
     }
     return moe::launch_gemm<TE>(g2, false, max_mt, 4 * cu_count(), st);
   }));

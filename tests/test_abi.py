@@ -36,6 +36,15 @@ def test_library_exports_every_declared_symbol():
     assert set(_declared()) <= exported
 
 
+def test_library_has_no_undefined_internal_symbols():
+    # a kernel whose host launch stub was not emitted links into a shared
+    # library silently and only fails when it is launched
+    out = subprocess.run(["nm", "-D", "-C", "--undefined-only", moe.lib_path()], capture_output=True,
+                         text=True)
+    bad = [l for l in out.stdout.splitlines() if "moe::" in l]
+    assert not bad, bad
+
+
 def test_status_strings_and_version():
     assert moe.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5, -6):
