@@ -1,6 +1,8 @@
 """Benchmark of the MI355X DeepSeekMoE layer forward (one GPU).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew|fp8]
+    python bench.py --copy-calibration          # plain copy of known size, for HBM counters
+    python bench.py --summarize-profile DIR     # text summary of rocprofv3 CSV output
 
 A step is one moe_forward call (router, node-limited top-8 selection, gates,
 permutation, routed + shared SwiGLU experts, gated combine) over one batch of
@@ -13,6 +15,10 @@ over the timed steps.  The CPU baseline is the float64 oracle timed on a
 bounded sample of the same workload on this host's cores.
 """
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,8 +32,92 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 
 
+# HBM traffic of the dominant kernel, from rocprofv3 counter runs of this
+# script (FETCH_SIZE and WRITE_SIZE, one run each, KiB per dispatch averaged
+# over the profiled steps), each scaled by bytes / counter for a plain copy of
+# known size (--copy-calibration).  The figures hold for the kernel sources
+# whose digest is recorded; after any change to them traffic reads null.
+COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
+                    "write_bytes_per_kib": 1073741824 / 1048576.0}
+MEASURED_TRAFFIC = {         # workload -> gemm_gate_up counters per launch
+    "decode": {"src_sha256": "42b576e62051a76ebe0cc65fba4a10f3592384f17a36cf38e74759a4ac3e25af",
+               "fetch_kib": 8099028.5, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "42b576e62051a76ebe0cc65fba4a10f3592384f17a36cf38e74759a4ac3e25af",
+                "fetch_kib": 12333410.7, "write_kib": 294912.3},
+}
+KERNEL_SOURCES = ("common.h", "kernels.h", "moe_api.cpp", "route_kernels.hip",
+                  "gemm_kernels.hip", "stream_gemm.hip", "tile_gemm.hip")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_layer_group_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of gemm_gate_up, or None when not measured for the current sources."""
+    t = MEASURED_TRAFFIC.get(workload)
+    if not t or not COPY_CALIBRATION or t["src_sha256"] != kernel_sources_sha256():
+        return None
+    return int(t["fetch_kib"] * COPY_CALIBRATION["fetch_bytes_per_kib"] +
+               t["write_kib"] * COPY_CALIBRATION["write_bytes_per_kib"])
+
+
+def copy_calibration(reps=5, nbytes=1 << 30):
+    """Known-size copies whose HBM counters calibrate FETCH_SIZE / WRITE_SIZE.
+
+    Two forms: torch's copy_ and an elementwise negation (one read and one
+    write stream of nbytes each); 1 GiB is far beyond the 256 MB last-level
+    cache, so every byte moves through HBM."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                            "reps": reps, "forms": ["copy_", "neg"]}}), flush=True)
+
+
+def summarize_profile(path):
+    """Text summary of rocprofv3 CSV output under path: kernel time statistics
+    (kernel_stats / kernel_trace) and per-dispatch counter averages."""
+    files = sorted(glob.glob(os.path.join(path, "**", "*.csv"), recursive=True))
+    for f in files:
+        rows = list(csv.DictReader(open(f)))
+        if f.endswith("kernel_stats.csv"):
+            print(f"# {os.path.relpath(f, path)}: kernel durations")
+            print(f"{'kernel':70s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s} {'total %':>8s}")
+            for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+                print(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                      f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} "
+                      f"{float(r['Percentage']):8.2f}")
+        elif f.endswith("counter_collection.csv"):
+            # counter names are truncated; the kernel id tells template instances apart
+            d = collections.defaultdict(list)
+            first = {}
+            for r in rows:
+                key = (r["Kernel_Name"], int(r["Kernel_Id"]), r["Counter_Name"])
+                d[key].append(float(r["Counter_Value"]))
+                first.setdefault(key, int(r["Dispatch_Id"]))
+            print(f"# {os.path.relpath(f, path)}: counters per dispatch")
+            print(f"{'kernel':40s} {'id':>6s} {'1st disp':>9s} {'counter':12s} {'dispatches':>10s} "
+                  f"{'mean':>14s} {'min':>14s} {'max':>14s}")
+            for key, v in sorted(d.items(), key=lambda kv: first[kv[0]]):
+                k, kid, cn = key
+                print(f"{k[:40]:40s} {kid:6d} {first[key]:9d} {cn:12s} {len(v):10d} "
+                      f"{sum(v) / len(v):14.1f} {min(v):14.1f} {max(v):14.1f}")
 
 
 def main():
@@ -40,9 +130,15 @@ def main():
                     help="skew workload: bias-update steps applied before timing")
     ap.add_argument("--cpu-tokens", type=int, default=12,
                     help="tokens in the CPU oracle sample (0 disables the CPU baseline)")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run plain copies of known size (for HBM counter calibration) and exit")
+    ap.add_argument("--summarize-profile", default=None, metavar="DIR",
+                    help="print a text summary of the rocprofv3 CSV files under DIR and exit")
     args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -56,6 +152,9 @@ def main():
     import synthetic as S
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     c = S.get_config(args.workload)
@@ -130,10 +229,7 @@ def main():
         bound, achieved, peak, unit = "hbm", gu_bytes / gu_s / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         bound, achieved, peak, unit = "mfma", gu_flops / gu_s / 1e12, MFMA_PEAK_TFLOPS[c.w_dtype], "TFLOP/s"
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        tr = json.load(open(args.traffic)).get(c.name, {})
-        traffic = tr.get("gemm_gate_up_bytes_per_launch")
+    traffic = measured_traffic(c.name)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "gemm_gate_up", "kernel_us": round(gu_s * 1e6, 2),
