@@ -75,7 +75,8 @@ enum moe_status {
  *   1 <= group_topn <= min(4, n_experts / n_groups), 1 <= topk_groups <= n_groups,
  *   1 <= topk <= min(32, topk_groups * n_experts / n_groups),
  *   n_shared in {0, 1}, hidden % 128 == 0, inter % 128 == 0,
- *   T * (topk + n_shared) < 2^31.
+ *   T * (topk + n_shared) < 2^31, T * max(hidden, inter) * sizeof(act) < 2^32,
+ *   and for E4M3 weights hidden <= 16384, inter <= 16384.
  * Dtypes (else MOE_ERR_DTYPE): (act, w) = (F32, F32), (BF16, BF16) or (BF16, E4M3).
  */
 typedef struct moe_cfg {
@@ -170,6 +171,21 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
  */
 int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float* bias,
                     float gamma, void* stream);
+
+/*
+ * Online activation quantisation to E4M3 (page "02 · DeepSeek-V3", §2.2: one
+ * scale per 1x128 tile of a token row, from the tile's max-abs value), the
+ * step moe_forward applies to x when the weights are E4M3.
+ *   x      device bfloat16 [rows][cols], cols % 128 == 0 (else MOE_ERR_SHAPE)
+ *   q      device uint8 [rows][cols]: OCP E4M3FN codes
+ *   scales device float [rows][cols/128]
+ * Per slice: scale = amax / 448 in float32 (1 when amax == 0); each code is
+ * the float32 quotient v / scale (IEEE division) rounded to nearest, ties to
+ * even, saturated at +-448.  rows == 0 returns MOE_OK without reading
+ * pointers.
+ */
+int moe_quantize_1x128(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                       void* stream);
 
 /*
  * Kernel timing instrumentation (off by default; not thread-safe).

@@ -245,9 +245,10 @@ ExpertSource = Callable[[int], Dict[str, np.ndarray]]
 
 def dequant_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Weights stored as e4m3 codes with one float32 scale per 128x128 block, as float64."""
-    v = e4m3_decode(codes)
+    v = e4m3_decode(np.asarray(codes))
     R, C = v.shape
-    return (v.reshape(R // 128, 128, C // 128, 128) * scales.astype(F64)[:, None, :, None]).reshape(R, C)
+    sc = np.asarray(scales, dtype=F64)
+    return (v.reshape(R // 128, 128, C // 128, 128) * sc[:, None, :, None]).reshape(R, C)
 
 
 def expert_f64(w: Dict[str, np.ndarray]):

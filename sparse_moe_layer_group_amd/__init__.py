@@ -18,7 +18,8 @@ import torch
 
 __all__ = ["F32", "BF16", "E4M3", "MoeError", "lib", "lib_path", "make_cfg", "cfg_from",
            "workspace_bytes", "alloc_workspace", "alloc_routing", "route", "forward",
-           "bias_update", "profile_enable", "profile_read", "status_string", "abi_version",
+           "bias_update", "quantize_1x128", "profile_enable", "profile_read", "status_string",
+           "abi_version",
            "EXPORTED_SYMBOLS"]
 
 F32, BF16, E4M3 = 0, 1, 2
@@ -27,7 +28,7 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8}
 
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_bias_update",
                     "moe_profile_enable", "moe_profile_read", "moe_profile_kernel_name",
-                    "moe_status_string", "moe_abi_version")
+                    "moe_status_string", "moe_abi_version", "moe_quantize_1x128")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
                                        I32]
         L.moe_profile_read.restype = I32
+        L.moe_quantize_1x128.argtypes = [P, I64, ctypes.c_int32, P, P, P]
+        L.moe_quantize_1x128.restype = I32
         L.moe_profile_kernel_name.argtypes = [I32]
         L.moe_profile_kernel_name.restype = ctypes.c_char_p
         _LIB = L
@@ -246,6 +249,17 @@ def forward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tens
                            ws.numel() if ws is not None else 0, _stream(stream))
     if rc != 0:
         raise MoeError(rc, "moe_forward")
+
+
+def quantize_1x128(x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """moe_quantize_1x128: bf16 [R][C] -> E4M3 codes (uint8 [R][C]) and float32 scales [R][C/128]."""
+    R, C = x.shape
+    _check(x, "x", torch.bfloat16, (R, C))
+    _check(q, "q", torch.uint8, (R, C))
+    _check(scales, "scales", torch.float32, (R, C // 128))
+    rc = lib().moe_quantize_1x128(_ptr(x), int(R), int(C), _ptr(q), _ptr(scales), _stream(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_quantize_1x128")
 
 
 def bias_update(cfg: _Cfg, T: int, counts: torch.Tensor, bias: torch.Tensor, gamma: float,

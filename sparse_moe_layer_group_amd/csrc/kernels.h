@@ -75,4 +75,30 @@ template <typename TE>
 hipError_t launch_combine(const TE* Y, const int32_t* slot, const float* gate, const TE* residual,
                           TE* y, int T, int K, int H, int TK, int S, hipStream_t st);
 
+// ---- FP8 E4M3 path (fp8_kernels.hip)
+// 1x128 activation quantisation: x bf16 [rows][C] -> codes [rows][C], scales [rows][C/128]
+hipError_t launch_quant_1x128(const bf16_t* x, long long rows, int C, uint8_t* q, float* scales,
+                              hipStream_t st);
+// block-scaled tiled GEMM, kTileM8-row tiles.  GATED: A = quantised x (rows
+// gathered through perm), out8/out_s = quantised SwiGLU output H and its 1x128
+// scales.  Down: A = quantised H, out16 = bf16 staged rows.
+struct TileArgs8 {
+  const uint8_t* a;           // E4M3 codes [rows][K]
+  const float* as;            // A scales [rows][K/128]
+  const uint8_t* w0;          // W_gate or W_down codes [E+S][N][K]
+  const uint8_t* w1;          // W_up (GATED)
+  const float* ws0;           // weight block scales [E+S][N/128][K/128]
+  const float* ws1;           // W_up block scales (GATED)
+  uint8_t* out8;              // GATED: H codes [rows][N]
+  bf16_t* out16;              // down: staged rows [rows][N]
+  float* out_s;               // GATED: H scales [rows][N/128]
+  const int32_t* perm;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* mt_start;    // [E+S+1] prefix of kTileM8-row tiles
+  int E, n_exp, T, TK, N, K;
+};
+constexpr int kTileM8 = 128;
+hipError_t launch_tile_gemm_fp8(const TileArgs8& g, bool gated, int max_mtiles, hipStream_t st);
+
 }  // namespace moe

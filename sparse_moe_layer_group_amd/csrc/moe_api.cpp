@@ -1,7 +1,8 @@
 // C ABI of the gfx950 MoE layer library: argument validation, workspace
 // carving and launch sequencing.  Every step of the layer runs in the HIP
-// kernels of route_kernels.hip and gemm_kernels.hip; this file only checks
-// arguments and enqueues them on the caller's stream.
+// kernels (route_kernels.hip, gemm_kernels.hip, stream_gemm.hip,
+// tile_gemm.hip, fp8_kernels.hip); this file only checks arguments and
+// enqueues them on the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -20,6 +21,7 @@ struct Layout {
   size_t wt3, P, idx, gate, counts, offsets, perm, slot, gap, masks, hist, base, chunk_start,
       mt_start;
   size_t hst, yst;
+  size_t hs, xq, xs;  // E4M3 weights: H scales, quantised x and its scales
   size_t route_total, total;
 };
 
@@ -55,7 +57,14 @@ Layout make_layout(const moe_cfg& c, int64_t T) {
   L.route_total = off;
   const size_t rows = TK + S * size_t(T);
   const size_t es = elem_bytes(c.act_dtype);
-  L.hst = take(rows * I * es);
+  if (c.w_dtype == MOE_E4M3) {
+    L.hst = take(rows * I);             // E4M3 codes of H
+    L.hs = take(rows * (I / 128) * 4);
+    L.xq = take(size_t(T) * H);
+    L.xs = take(size_t(T) * (H / 128) * 4);
+  } else {
+    L.hst = take(rows * I * es);
+  }
   L.yst = take(rows * H * es);
   L.total = off;
   return L;
@@ -73,13 +82,20 @@ int validate_cfg(const moe_cfg* c) {
   if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_SHAPE;
   const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32;
   const bool bf16 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_BF16;
-  if (!f32 && !bf16) return MOE_ERR_DTYPE;
+  const bool fp8 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_E4M3;
+  if (!f32 && !bf16 && !fp8) return MOE_ERR_DTYPE;
+  // the E4M3 GEMM holds at most 128 weight scales along K per wave
+  if (fp8 && (c->hidden > 16384 || c->inter > 16384)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
+// T bounds: row counts fit int32, and one expert's activation rows (at most T)
+// span less than 4 GiB, the reach of the tiled GEMMs' 32-bit offsets.
 int validate_T(const moe_cfg* c, int64_t T) {
   if (T < 0) return MOE_ERR_SHAPE;
   if (T * int64_t(c->topk + c->n_shared) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  const int64_t width = std::max<int64_t>(c->hidden, c->inter) * int64_t(elem_bytes(c->act_dtype));
+  if (T * width >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -102,9 +118,12 @@ int check_device() {
 
 // ---------------------------------------------------------------- instrumentation
 
-enum Slot { K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_NSLOTS };
-const char* const kSlotNames[K_NSLOTS] = {"router_logits", "select", "permute", "gemm_gate_up",
-                                          "gemm_down", "combine", "bias_update"};
+enum Slot {
+  K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_QUANT, K_NSLOTS
+};
+const char* const kSlotNames[K_NSLOTS] = {"router_logits", "select",  "permute",
+                                          "gemm_gate_up",  "gemm_down", "combine",
+                                          "bias_update",   "quantize"};
 
 struct Prof {
   bool on = false;
@@ -156,16 +175,19 @@ struct RoutePtrs {
 // rest to the tiled GEMM.  When the average expert has <= 32 rows (decode)
 // every expert streams, the shared one included.
 int stream_max_rows(const moe_cfg& c, int T) {
-  if (c.act_dtype != MOE_BF16) return -1;
+  if (c.act_dtype != MOE_BF16 || c.w_dtype != MOE_BF16) return -1;
   const long long avg32 = (long long)T * c.topk;
   return (avg32 <= 32LL * c.n_experts) ? 0x7fffffff : 64;
 }
 
-// bf16 layers use the 256-row LDS-pipelined tiled GEMM; the float32 layer the
-// 64x64 tiled GEMM.
-bool use_big_tiles(const moe_cfg& c) { return c.act_dtype == MOE_BF16; }
+// bf16 layers use the LDS-pipelined tiled GEMM (kTileM rows), E4M3 weights its
+// block-scaled fp8 form (kTileM8 rows), the float32 layer the 64x64 tiled GEMM.
+bool use_big_tiles(const moe_cfg& c) { return c.act_dtype == MOE_BF16 && c.w_dtype == MOE_BF16; }
 
-int tile_rows(const moe_cfg& c) { return use_big_tiles(c) ? moe::kTileM : moe::gemm_tile_m(); }
+int tile_rows(const moe_cfg& c) {
+  if (c.w_dtype == MOE_E4M3) return moe::kTileM8;
+  return use_big_tiles(c) ? moe::kTileM : moe::gemm_tile_m();
+}
 
 int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const float* bias,
               const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
@@ -289,6 +311,40 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
   return MOE_OK;
 }
 
+// E4M3 weights: quantise x per 1x128 slice, block-scaled gate/up GEMM with
+// the SwiGLU output quantised in its epilogue, block-scaled down GEMM, combine.
+int run_experts_fp8(const moe_cfg& c, int T, const bf16_t* x, const moe_experts* w,
+                    const bf16_t* residual, bf16_t* y, const RoutePtrs& r, void* ws,
+                    const Layout& L, hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
+  const int TK = T * K;
+  const int bm = moe::kTileM8;
+  const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  float* xs = at<float>(ws, L.xs);
+  uint8_t* hq = at<uint8_t>(ws, L.hst);
+  float* hs = at<float>(ws, L.hs);
+  bf16_t* yst = at<bf16_t>(ws, L.yst);
+  const int32_t* mt_start = at<int32_t>(ws, L.mt_start);
+  MOE_TRY(timed(K_QUANT, st, [&] { return moe::launch_quant_1x128(x, T, H, xq, xs, st); }));
+  MOE_TRY(timed(K_GATEUP, st, [&] {
+    moe::TileArgs8 ta{xq, xs, static_cast<const uint8_t*>(w->w_gate),
+                      static_cast<const uint8_t*>(w->w_up), w->s_gate, w->s_up, hq, nullptr, hs,
+                      r.perm, r.counts, r.offsets, mt_start, E, E + S, T, TK, I, H};
+    return moe::launch_tile_gemm_fp8(ta, true, max_mt, st);
+  }));
+  MOE_TRY(timed(K_DOWN, st, [&] {
+    moe::TileArgs8 ta{hq, hs, static_cast<const uint8_t*>(w->w_down), nullptr, w->s_down, nullptr,
+                      nullptr, yst, nullptr, r.perm, r.counts, r.offsets, mt_start, E, E + S, T, TK,
+                      H, I};
+    return moe::launch_tile_gemm_fp8(ta, false, max_mt, st);
+  }));
+  MOE_TRY(timed(K_COMBINE, st, [&] {
+    return moe::launch_combine<bf16_t>(yst, r.slot, r.gate, residual, y, T, K, H, TK, S, st);
+  }));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -373,6 +429,8 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   if (x == nullptr || w_router == nullptr || bias == nullptr || w == nullptr || y == nullptr)
     return MOE_ERR_NULL;
   if (w->w_gate == nullptr || w->w_up == nullptr || w->w_down == nullptr) return MOE_ERR_NULL;
+  if (cfg->w_dtype == MOE_E4M3 && (w->s_gate == nullptr || w->s_up == nullptr || w->s_down == nullptr))
+    return MOE_ERR_NULL;
   const Layout L = make_layout(*cfg, T);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if ((rc = check_device()) != MOE_OK) return rc;
@@ -380,6 +438,10 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   const RoutePtrs r = route_ptrs(out, ws, L);
   rc = run_route(*cfg, int(T), x, w_router, bias, r, ws, L, st);
   if (rc != MOE_OK) return rc;
+  if (cfg->w_dtype == MOE_E4M3)
+    return run_experts_fp8(*cfg, int(T), static_cast<const bf16_t*>(x), w,
+                           static_cast<const bf16_t*>(residual), static_cast<bf16_t*>(y), r, ws, L,
+                           st);
   if (cfg->act_dtype == MOE_BF16)
     return run_experts<bf16_t>(*cfg, int(T), static_cast<const bf16_t*>(x), w,
                                static_cast<const bf16_t*>(residual), static_cast<bf16_t*>(y), r,
@@ -387,6 +449,21 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   return run_experts<float>(*cfg, int(T), static_cast<const float*>(x), w,
                             static_cast<const float*>(residual), static_cast<float*>(y), r, ws, L,
                             st);
+}
+
+int moe_quantize_1x128(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                       void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_ERR_SHAPE;
+  if (rows * int64_t(cols) >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || q == nullptr || scales == nullptr) return MOE_ERR_NULL;
+  int rc = check_device();
+  if (rc != MOE_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_TRY(timed(K_QUANT, st, [&] {
+    return moe::launch_quant_1x128(static_cast<const bf16_t*>(x), rows, cols, q, scales, st);
+  }));
+  return MOE_OK;
 }
 
 int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float* bias,

@@ -132,8 +132,11 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
   // w + NWAVE i, B rows 16(w*BCPW + i)..); lane l writes LDS bytes 16 l of that
   // 1 KB, i.e. row r0 + l/4 at swizzled position l%4, which holds logical chunk
   // swz(row, l%4).  32-bit byte offsets from uniform base pointers.
+  // (A offsets stay below T * K * 2 bytes: x rows are token ids < T; staged
+  // rows are addressed from the expert's first row)
   uint32_t aoff[ACPW], boff[BCPW];
-  const char* __restrict__ abase = reinterpret_cast<const char*>(g.a);
+  const char* __restrict__ abase =
+      reinterpret_cast<const char*>(GATED ? g.a : g.a + (size_t)row_base * K);
   const char* __restrict__ wb0 = reinterpret_cast<const char*>(g.w0 + (size_t)e * g.N * K);
   const char* __restrict__ wb1 =
       GATED ? reinterpret_cast<const char*>(g.w1 + (size_t)e * g.N * K) : wb0;
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
     const int m = m0 + min(r, rows - 1);  // rows past the count re-read a valid row
     int arow;
     if (GATED) arow = shared ? m : g.perm[row_base + m];
-    else arow = row_base + m;
+    else arow = m;
     aoff[i] = (uint32_t(arow) * uint32_t(K) + uint32_t(chunk * 8)) * 2u;
   }
 #pragma unroll

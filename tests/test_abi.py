@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(moe.lib_path()),
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_symbols():
@@ -143,3 +143,28 @@ def test_binding_has_no_cpu_fallback():
             src = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in src.replace("the oracle", ""), fn
             assert "synthetic" not in src, fn
+
+
+def test_fp8_configuration_checks():
+    L = moe.lib()
+    c = _v3(w_dtype=moe.E4M3)
+    assert moe.workspace_bytes(c, 16) > 0          # (BF16, E4M3) is accepted
+    # E4M3 workspace: codes of x and H plus their 1x128 scales, bf16 staging of Y
+    assert moe.workspace_bytes(c, 4096) >= 4096 * 7168 + 4096 * 9 * (2048 + 7168 * 2)
+    one = ctypes.c_void_p(1)
+    ex = moe._Experts(1, 1, 1, None, 1, 1)           # s_gate missing
+    assert L.moe_forward(ctypes.byref(c), 16, one, one, one, ctypes.byref(ex), None, one, None, one,
+                         1 << 40, None) == -1
+    assert moe.workspace_bytes(_v3(w_dtype=moe.E4M3, hidden=16384 + 128), 16) == 0
+    # one expert's activation rows must span < 4 GiB
+    assert moe.workspace_bytes(_v3(), 299000) > 0
+    assert moe.workspace_bytes(_v3(), 300000) == 0
+
+
+def test_quantize_argument_checks():
+    L = moe.lib()
+    one = ctypes.c_void_p(1)
+    assert L.moe_quantize_1x128(one, 4, 100, one, one, None) == -2     # cols % 128
+    assert L.moe_quantize_1x128(one, -1, 128, one, one, None) == -2
+    assert L.moe_quantize_1x128(None, 0, 128, None, None, None) == 0    # no rows: nothing read
+    assert L.moe_quantize_1x128(one, 4, 128, None, one, None) == -1
