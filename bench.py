@@ -126,8 +126,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "fp8"])
-    ap.add_argument("--skew-step", type=int, default=0,
-                    help="skew workload: bias-update steps applied before timing")
+    ap.add_argument("--skew-steps", type=int, default=200,
+                    help="skew workload: bias-update steps (forward timed at first, middle, last)")
     ap.add_argument("--cpu-tokens", type=int, default=12,
                     help="tokens in the CPU oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -173,41 +173,68 @@ def main():
     out = moe.alloc_routing(cfg, T, dev)
     ws = moe.alloc_workspace(cfg, T, dev)
 
-    if c.name == "skew" and args.skew_step > 0:
-        wsr = moe.alloc_workspace(cfg, T, dev)
-        for st in range(args.skew_step):
-            xs = S.gen_x(c, step=st, device=dev)
-            moe.route(cfg, xs, wr, b, out, wsr)
-            moe.bias_update(cfg, T, out["counts"], b, c.gamma)
-        torch.cuda.synchronize()
-        log(f"skew: applied {args.skew_step} bias steps")
-
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        moe.forward(cfg, x, wr, b, ex, y, ws, out=out, stream=stream)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
 
-    moe.profile_read()           # clear
-    moe.profile_enable(True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        moe.forward(cfg, x, wr, b, ex, y, ws, out=out, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall1 = time.perf_counter()
-    moe.profile_enable(False)
-    kern = moe.profile_read()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (wall {1e3 * (wall1 - wall0) / args.steps:.4f})")
-    for k, (ms, n) in kern.items():
-        if n:
-            log(f"  {k:14s} {ms / n * 1e3:9.1f} us/launch  ({n} launches)")
+    def timed_forward(xb, bb):
+        """Warmup, then args.steps forwards timed with HIP events on the stream."""
+        for _ in range(args.warmup):
+            moe.forward(cfg, xb, wr, bb, ex, y, ws, out=out, stream=stream)
+        torch.cuda.synchronize()
+        moe.profile_read()           # clear
+        moe.profile_enable(True)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            moe.forward(cfg, xb, wr, bb, ex, y, ws, out=out, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall1 = time.perf_counter()
+        moe.profile_enable(False)
+        kern = moe.profile_read()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        log(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {1e3 * (wall1 - wall0) / args.steps:.4f})")
+        for k, (kms, n) in kern.items():
+            if n:
+                log(f"  {k:14s} {kms / n * 1e3:9.1f} us/launch  ({n} launches)")
+        return ms, kern
+
+    skew = None
+    if c.name == "skew":
+        # the loss-free bias loop: step st routes a fresh batch with the bias of
+        # st earlier updates, then updates it from that batch's loads; the
+        # forward is timed at checkpoint steps before their update
+        checkpoints = sorted(set(min(v, args.skew_steps - 1) for v in (0, args.skew_steps // 2,
+                                                                       args.skew_steps - 1)))
+        ratios, at = [], {}
+        wsr = moe.alloc_workspace(cfg, T, dev)
+        outr = moe.alloc_routing(cfg, T, dev)
+        for st in range(args.skew_steps):
+            xs = S.gen_x(c, step=st, device=dev)
+            if st in checkpoints:
+                log(f"skew: step {st}")
+                ms_c, kern_c = timed_forward(xs, b)
+                at[st] = (ms_c, kern_c, out["counts"].clone(), b.clone())
+            moe.route(cfg, xs, wr, b, outr, wsr)
+            moe.bias_update(cfg, T, outr["counts"], b, c.gamma)
+            cn = outr["counts"].cpu().numpy().astype(np.float64)
+            ratios.append(float(cn.max() / cn.mean()))
+        torch.cuda.synchronize()
+        log(f"skew: {args.skew_steps} bias steps; max/mean load at step 0 {ratios[0]:.2f}, "
+            f"step {args.skew_steps // 2} {ratios[args.skew_steps // 2]:.2f}, last {ratios[-1]:.2f}")
+        # the reported figures are those of the last checkpoint (its batch and bias)
+        ms_step, kern, counts_t, b = at[checkpoints[-1]]
+        out["counts"].copy_(counts_t)
+        x = S.gen_x(c, step=checkpoints[-1], device=dev)
+        skew = {"steps": args.skew_steps, "gamma": c.gamma,
+                "max_over_mean_load_per_step": [round(v, 3) for v in ratios],
+                "checkpoints": {str(k): {"ms_per_step": round(v[0], 4),
+                                         "tokens_per_s": round(T / (v[0] / 1e3), 1)}
+                                for k, v in at.items()}}
+    else:
+        ms_step, kern = timed_forward(x, b)
 
     counts = out["counts"].cpu().numpy().astype(np.int64)
     active = int((counts > 0).sum())
@@ -223,7 +250,11 @@ def main():
     # dominant kernel: gate/up grouped GEMM (two of the three expert matrices)
     gu_ms, gu_n = kern["gemm_gate_up"]
     gu_s = gu_ms / max(gu_n, 1) / 1e3
-    gu_bytes = n_exp * (2 * H * I * wbytes + 2 * scale_bytes // 3) + T * H * abytes + rows * I * abytes
+    if c.w_dtype == "e4m3":   # reads x and writes H as E4M3 codes with 1x128 scales
+        gu_bytes = (n_exp * (2 * H * I * wbytes + 2 * scale_bytes // 3) + T * H + T * (H // 128) * 4
+                    + rows * I + rows * (I // 128) * 4)
+    else:
+        gu_bytes = n_exp * (2 * H * I * wbytes + 2 * scale_bytes // 3) + T * H * abytes + rows * I * abytes
     gu_flops = rows * 2 * 2 * H * I
     if c.name == "decode" or c.name == "skew" or c.name == "fp8":
         bound, achieved, peak, unit = "hbm", gu_bytes / gu_s / 1e9, HBM_PEAK_GBS, "GB/s"
@@ -267,6 +298,7 @@ def main():
         "roofline": roofline,
         "layer": layer,
         "cpu_baseline": cpu,
+        **({"skew": skew} if skew is not None else {}),
     }
     print(json.dumps(res), flush=True)
 
