@@ -16,7 +16,8 @@ and section:
          13, 15); §1.4 auxiliary-loss-free balancing (Eq 16); §2.2 FP8
          fine-grained quantisation; §5.1 deployment (shared expert as an
          always-selected expert).
-  [DEP]  "DeepSeek-V3 MoE cost and deployment" audit page (FP8 weight release).
+  [DEP]  "DeepSeek-V3 复盘：MoE、MLA、FP8 与低成本叙事如何验算" (audit of the
+         report's cost and deployment claims; the released weights are FP8).
 
 The display equations of [V3] are missing from the extracted text; every
 formula below is rebuilt from the surrounding prose, and each reading taken
