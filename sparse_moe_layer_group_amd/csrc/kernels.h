@@ -9,7 +9,8 @@ namespace moe {
 typedef uint16_t bf16_t;
 
 // ---- routing (route_kernels.hip)
-int router_ksplit(int H);
+int router_ksplit(int H);                                // partials the workspace holds
+int router_partials(int T, int H, int E, bool x_bf16);  // partials launch_router writes
 size_t router_split_bytes(int H, int E);
 hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt3, float* P,
                          int T, int H, int E, hipStream_t st);
@@ -49,6 +50,7 @@ struct StreamArgs {
   const int32_t* chunk_start; // [E+S+1] prefix of 16-row chunks of streamed experts
   int E, n_exp, T, TK, N, K;
 };
+constexpr int kMaxStreamExperts = 1024;  // n_exp bound of the streaming GEMM's LDS tables
 hipError_t launch_stream_gemm(const StreamArgs& g, bool gated, int n_blocks, hipStream_t st);
 
 // LDS-tiled GEMM for experts with many rows (tile_gemm.hip), bf16 only;
@@ -64,7 +66,10 @@ struct TileArgs {
   const int32_t* mt_start;    // [E+S+1] prefix of kTileM-row tiles of tiled experts
   int E, n_exp, T, TK, N, K;
 };
-constexpr int kTileM = 320;
+#ifndef MOE_TILE_MBW
+#define MOE_TILE_MBW 5  // 32-row MFMA blocks per wave of the tiled GEMM (2 waves along M)
+#endif
+constexpr int kTileM = 64 * MOE_TILE_MBW;
 hipError_t launch_tile_gemm(const TileArgs& g, bool gated, int max_mtiles, hipStream_t st);
 
 int gemm_tile_m();

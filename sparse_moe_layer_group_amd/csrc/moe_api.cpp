@@ -198,7 +198,8 @@ int run_route(const moe_cfg& c, int T, const void* x, const float* wr, const flo
                               st);
   }));
   MOE_TRY(timed(K_SELECT, st, [&] {
-    return moe::launch_select(P, moe::router_ksplit(H), bias, T, E, c.n_groups, c.topk_groups, K,
+    return moe::launch_select(P, moe::router_partials(T, H, E, c.act_dtype == MOE_BF16), bias, T,
+                              E, c.n_groups, c.topk_groups, K,
                               c.group_topn, r.idx, r.gate, r.gap, st);
   }));
   MOE_TRY(timed(K_PERMUTE, st, [&] {

@@ -4,6 +4,8 @@
 //
 // Method: "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token", §1.3 (Eq 13, 15)
 // and §1.4 (Eq 16).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -109,11 +111,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TA* __restrict
 // Every float32 router weight is the exact sum of three bfloat16 parts
 // (hi = top 8 significant bits, mid = next 8, lo = rest, each a truncation
 // remainder), so x * w = x*hi + x*mid + x*lo exactly for a bfloat16 x and
-// three bf16 MFMAs give the float32 products with float32 accumulation.
-// router_split writes the parts transposed, Wt3[3][E][H], so both MFMA
-// operands are K-contiguous.
+// bf16 MFMAs give the float32 products with float32 accumulation.  The logits
+// are then one bf16 GEMM with K = 3H: router_split writes, for each expert e,
+// the row [hi(W_r[:,e]) | mid(W_r[:,e]) | lo(W_r[:,e])] (Wt3 [E][3H],
+// K-contiguous), and the activation row is read three times.
 // ============================================================================
 
+// 64 x 64 (k, e) tile through LDS; each thread then writes 8 consecutive k of
+// one expert and one part as a 16-byte vector.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
                                                            bf16_t* __restrict__ wt3, int H,
                                                            int E) {
@@ -125,21 +130,159 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     tile[kk][ee] = (k < H && e < E) ? wr[(size_t)k * E + e] : 0.f;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int ee = i / 64, kk = i % 64;
-    const int k = k0 + kk, e = e0 + ee;
-    if (k >= H || e >= E) continue;
-    const float w = tile[kk][ee];
-    const uint32_t u = __float_as_uint(w);
-    const uint32_t hi = u & 0xffff0000u;
-    const float r1 = w - __uint_as_float(hi);              // exact
-    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
-    const float r2 = r1 - __uint_as_float(mid);            // exact, fits 8 bits
-    const size_t o = (size_t)e * H + k;
-    wt3[o] = bf16_t(hi >> 16);
-    wt3[(size_t)E * H + o] = bf16_t(mid >> 16);
-    wt3[2 * (size_t)E * H + o] = bf16_t(__float_as_uint(r2) >> 16);
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int ee = i / 8, kg = (i % 8) * 8;
+    const int e = e0 + ee;
+    if (e >= E || k0 + kg >= H) continue;  // H % 128 == 0: a group is all in or all out
+    u32x4 hi4, mid4, lo4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t part[3][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float w = tile[kg + 2 * q + h][ee];
+        const uint32_t u = __float_as_uint(w);
+        const uint32_t hi = u & 0xffff0000u;
+        const float r1 = w - __uint_as_float(hi);              // exact
+        const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(mid);            // exact, fits 8 bits
+        part[0][h] = hi >> 16;
+        part[1][h] = mid >> 16;
+        part[2][h] = __float_as_uint(r2) >> 16;
+      }
+      hi4[q] = part[0][0] | (part[0][1] << 16);
+      mid4[q] = part[1][0] | (part[1][1] << 16);
+      lo4[q] = part[2][0] | (part[2][1] << 16);
+    }
+    bf16_t* row = wt3 + (size_t)e * 3 * H + k0 + kg;
+    *reinterpret_cast<u32x4*>(row) = hi4;
+    *reinterpret_cast<u32x4*>(row + H) = mid4;
+    *reinterpret_cast<u32x4*>(row + 2 * H) = lo4;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Router logits for large batches: an LDS-tiled bf16 GEMM over K = 3H.
+// Workgroup tile 128 tokens x 256 experts, split along K into `chunks` parts
+// (P[c][t][e], added in order by the select kernel).  K steps of 32 staged by
+// direct global->LDS copies three steps ahead into four stages (24 KB each);
+// the activation row of step kt is x[t][kt*32 mod H ..].  Eight waves in
+// 2 x 4, each 64 x 64 as 2 x 2 MFMA 32x32x16 blocks.  Staged rows are 64 bytes
+// (four 16-byte chunks at chunk ^ ((row/2) % 4)).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int RT_TBM = 128, RT_TBN = 256, RT_TBK = 32, RT_NSTAGE = 4;
+constexpr int RT_NWAVE = 8, RT_WN = 4;
+constexpr int RT_ASTAGE = RT_TBM * RT_TBK, RT_BSTAGE = RT_TBN * RT_TBK;  // bf16 elements
+typedef __attribute__((address_space(3))) void rt_lds_void;
+MOE_DEV int rt_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+}  // namespace
+
+__global__ __launch_bounds__(512, 1) void router_tile_kernel(const bf16_t* __restrict__ x,
+                                                             const bf16_t* __restrict__ wt3,
+                                                             float* __restrict__ P, int T, int H,
+                                                             int E, int steps_per_chunk) {
+  constexpr int ACPW = RT_TBM / 16 / RT_NWAVE;   // 1 KB copies of A per wave per step
+  constexpr int BCPW = RT_TBN / 16 / RT_NWAVE;
+  constexpr int CPS = ACPW + BCPW;
+  static_assert(ACPW >= 1 && BCPW >= 1, "tile");
+  __shared__ __attribute__((aligned(16))) bf16_t As[RT_NSTAGE * RT_ASTAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[RT_NSTAGE * RT_BSTAGE];
+  const int t0 = blockIdx.x * RT_TBM, e0 = blockIdx.y * RT_TBN, c = blockIdx.z;
+  const int nsteps_all = 3 * H / RT_TBK;
+  const int kt0 = c * steps_per_chunk;
+  const int nk = min(steps_per_chunk, nsteps_all - kt0);
+  const int rows = min(RT_TBM, T - t0), cols = min(RT_TBN, E - e0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / RT_WN, wn = wave % RT_WN;
+  const int spp = H / RT_TBK;  // steps per part
+
+  uint32_t aoff[ACPW], boff[BCPW];
+#pragma unroll
+  for (int i = 0; i < ACPW; ++i) {
+    const int r = 16 * (wave * ACPW + i) + (lane >> 2);
+    const int t = t0 + min(r, rows - 1);
+    aoff[i] = (uint32_t(t) * uint32_t(H) + uint32_t(rt_swz(r, lane & 3) * 8)) * 2u;
+  }
+  const char* __restrict__ bbase = reinterpret_cast<const char*>(wt3 + (size_t)e0 * 3 * H);
+#pragma unroll
+  for (int i = 0; i < BCPW; ++i) {
+    const int r = 16 * (wave * BCPW + i) + (lane >> 2);
+    const int e = min(r, cols - 1);
+    boff[i] = (uint32_t(e) * uint32_t(3 * H) + uint32_t(rt_swz(r, lane & 3) * 8)) * 2u;
+  }
+  const char* __restrict__ abase = reinterpret_cast<const char*>(x);
+
+  auto copy_step = [&](int j) {
+    const int kt = kt0 + min(j, nk - 1);
+    const int part = kt / spp;
+    const uint32_t ka = uint32_t((kt - part * spp) * RT_TBK * 2);
+    const uint32_t kb = uint32_t(kt * RT_TBK * 2);
+    const int stage = j % RT_NSTAGE;
+    bf16_t* a = As + stage * RT_ASTAGE + (16 * ACPW * wave) * RT_TBK;
+    bf16_t* b = Bs + stage * RT_BSTAGE + (16 * BCPW * wave) * RT_TBK;
+#pragma unroll
+    for (int i = 0; i < ACPW; ++i)
+      __builtin_amdgcn_global_load_lds(abase + (aoff[i] + ka), (rt_lds_void*)(a + 16 * i * RT_TBK),
+                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BCPW; ++i)
+      __builtin_amdgcn_global_load_lds(bbase + (boff[i] + kb), (rt_lds_void*)(b + 16 * i * RT_TBK),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int arow0 = wm * 64 + (lane & 31), brow0 = wn * 64 + (lane & 31);
+  auto frag = [&](const bf16_t* base, int row, int chunk) {
+    return *reinterpret_cast<const bf16x8*>(base + row * RT_TBK + (rt_swz(row, chunk) << 3));
+  };
+
+  constexpr int VMWAIT = (RT_NSTAGE - 2) * CPS;
+  constexpr int WAITIMM = (VMWAIT & 15) | ((VMWAIT >> 4) << 14) | 0x70 | 0xf00;
+#pragma unroll
+  for (int p = 0; p < RT_NSTAGE - 1; ++p) copy_step(p);
+  for (int j = 0; j < nk; ++j) {
+    __builtin_amdgcn_s_waitcnt(WAITIMM);  // this wave's copies of step j are done
+    __builtin_amdgcn_s_barrier();
+    copy_step(j + RT_NSTAGE - 1);
+    const bf16_t* a = As + (j % RT_NSTAGE) * RT_ASTAGE;
+    const bf16_t* b = Bs + (j % RT_NSTAGE) * RT_BSTAGE;
+#pragma unroll
+    for (int s16 = 0; s16 < RT_TBK / 16; ++s16) {
+      const int ch = 2 * s16 + (lane >> 5);
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = frag(a, arow0 + 32 * i, ch);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) bf[i] = frag(b, brow0 + 32 * i, ch);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no copy left in flight
+  __builtin_amdgcn_s_barrier();
+
+  float* Pc = P + (size_t)c * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = wn * 64 + 32 * jj + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r < rows && col < cols) Pc[(size_t)(t0 + r) * E + e0 + col] = acc[i][jj][v];
+      }
+    }
 }
 
 // P[ks][t][e] for one K chunk: wave tile 32 tokens x 32 experts (2 x 2 MFMA
@@ -164,9 +307,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
     const int t = t0 + i * 16 + (lane & 15);
     arow[i] = (t < T) ? x + (size_t)t * H + koff : nullptr;
     const int e = e0 + i * 16 + (lane & 15);
-    brow[i] = (e < E) ? wt3 + (size_t)e * H + koff : nullptr;
+    brow[i] = (e < E) ? wt3 + (size_t)e * 3 * H + koff : nullptr;
   }
-  const size_t part = (size_t)E * H;
+  const size_t part = (size_t)H;
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -499,6 +642,23 @@ int router_ksplit(int H) {
   return (H + chunk - 1) / chunk;
 }
 
+// Large bf16 batches use the tiled router: K = 3H split into chunks so that
+// about 256 workgroups run (at most router_ksplit(H), the partials the
+// workspace holds).  Returns the number of partials written (0: not used).
+static int router_tile_chunks(int T, int H, int E) {
+  if (T < 2048) return 0;
+  const int tiles = ((T + RT_TBM - 1) / RT_TBM) * ((E + RT_TBN - 1) / RT_TBN);
+  int chunks = std::max(1, std::min(router_ksplit(H), 256 / tiles));
+  const int nsteps = 3 * H / RT_TBK;
+  const int spc = (nsteps + chunks - 1) / chunks;
+  return (nsteps + spc - 1) / spc;  // no empty chunk
+}
+
+int router_partials(int T, int H, int E, bool x_bf16) {
+  const int tc = x_bf16 ? router_tile_chunks(T, H, E) : 0;
+  return tc > 0 ? tc : router_ksplit(H);
+}
+
 size_t router_split_bytes(int H, int E) { return (size_t)3 * H * E * sizeof(bf16_t); }
 
 hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt3, float* P,
@@ -510,6 +670,15 @@ hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt
                        wr, wt3, H, E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    const int tc = router_tile_chunks(T, H, E);
+    if (tc > 0) {
+      const int nsteps = 3 * H / RT_TBK;
+      const int spc = (nsteps + tc - 1) / tc;
+      hipLaunchKernelGGL(router_tile_kernel,
+                         dim3((T + RT_TBM - 1) / RT_TBM, (E + RT_TBN - 1) / RT_TBN, tc), dim3(512),
+                         0, st, static_cast<const bf16_t*>(x), wt3, P, T, H, E, spc);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 31) / 32, (E + 127) / 128, ks), dim3(256), 0,
                        st, static_cast<const bf16_t*>(x), wt3, P, T, H, E, chunk);
   } else {

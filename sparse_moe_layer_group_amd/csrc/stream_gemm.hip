@@ -65,12 +65,28 @@ MOE_DEV void mma_step(f32x4 (&acc)[NT], const u32x4 (&b)[NT][2], const u32x4 (&a
 
 }  // namespace
 
+// (expert, row base, rows, slice, first row) of a task
+struct StreamTask {
+  int e, row_base, m0, rows, slice;
+};
+
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
+  // chunk prefix, counts and offsets in LDS: the per-task expert search must
+  // not wait on dependent global loads between two tasks' weight streams
+  __shared__ int cs_s[kMaxStreamExperts + 1];
+  __shared__ int cnt_s[kMaxStreamExperts], off_s[kMaxStreamExperts];
+  for (int i = threadIdx.x; i <= g.n_exp; i += blockDim.x) cs_s[i] = g.chunk_start[i];
+  for (int i = threadIdx.x; i < g.E; i += blockDim.x) {
+    cnt_s[i] = g.counts[i];
+    off_s[i] = g.offsets[i];
+  }
+  __syncthreads();
+
   const int lane = threadIdx.x & 63;
   const int cols = GATED ? 64 : 128;
   const int n_slices = g.N / cols;
-  const int n_tasks = g.chunk_start[g.n_exp] * n_slices;
+  const int n_tasks = cs_s[g.n_exp] * n_slices;
   const int nsteps = g.K / SK;
   const int koff0 = 16 * (lane >> 4);
 
@@ -78,37 +94,48 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
   const int rounds = (n_tasks + slots - 1) / slots;
   const int active = rounds > 0 ? (n_tasks + rounds - 1) / rounds : 0;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= active) return;  // no barriers in this kernel
-  for (int task = wid; task < n_tasks; task += active) {
+  if (wid >= active) return;  // no barriers below
+
+  auto decode = [&](int task) {
     // task -> (expert, slice, row chunk); tasks of an expert are slice-major
     const int cidx = task / n_slices;
     int lo = 0, hi = g.n_exp - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (g.chunk_start[mid] <= cidx) lo = mid;
+      if (cs_s[mid] <= cidx) lo = mid;
       else hi = mid - 1;
     }
-    const int e = lo;
-    const bool shared = e >= g.E;
-    const int cnt = shared ? g.T : g.counts[e];
-    const int row_base = shared ? g.TK + (e - g.E) * g.T : g.offsets[e];
+    StreamTask t;
+    t.e = lo;
+    const bool shared = lo >= g.E;
+    const int cnt = shared ? g.T : cnt_s[lo];
+    t.row_base = shared ? g.TK + (lo - g.E) * g.T : off_s[lo];
     const int nch = (cnt + 15) >> 4;
-    const int local = task - g.chunk_start[e] * n_slices;
-    const int slice = local / nch;
-    const int chunk = local - slice * nch;
-    const int m0 = chunk * 16;
-    const int rows = min(16, cnt - m0);
+    const int local = task - cs_s[lo] * n_slices;
+    t.slice = local / nch;
+    t.m0 = (local - t.slice * nch) * 16;
+    t.rows = min(16, cnt - t.m0);
+    return t;
+  };
+  // activation row of this lane (every lane a valid row of the chunk)
+  auto a_row = [&](const StreamTask& t) {
+    const int m = t.m0 + min(lane & 15, t.rows - 1);
+    if (GATED) return (t.e >= g.E) ? m : g.perm[t.row_base + m];
+    return t.row_base + m;
+  };
 
-    const bf16_t* arow;
-    {
-      const int m = m0 + min(lane & 15, rows - 1);   // a valid row for every lane
-      if (GATED) {
-        const int tok = shared ? m : g.perm[row_base + m];
-        arow = g.a + (size_t)tok * g.K + koff0;
-      } else {
-        arow = g.a + (size_t)(row_base + m) * g.K + koff0;
-      }
-    }
+  StreamTask cur = decode(wid);
+  int cur_row = a_row(cur);
+  for (int task = wid; task < n_tasks; task += active) {
+    // the next task's description and token row are fetched now and arrive
+    // while this task streams
+    const int ntask = task + active < n_tasks ? task + active : task;
+    const StreamTask nxt = decode(ntask);
+    const int nxt_row = a_row(nxt);
+
+    const int e = cur.e, row_base = cur.row_base, m0 = cur.m0, rows = cur.rows;
+    const int slice = cur.slice;
+    const bf16_t* arow = g.a + (size_t)cur_row * g.K + koff0;
     const bf16_t* brow[NT];
     const bf16_t* w0 = g.w0 + (size_t)e * g.N * g.K;
     if (GATED) {
@@ -163,10 +190,13 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
         *reinterpret_cast<u32x4*>(dst + c) = pk;
       }
     }
+    cur = nxt;
+    cur_row = nxt_row;
   }
 }
 
 hipError_t launch_stream_gemm(const StreamArgs& g, bool gated, int n_blocks, hipStream_t st) {
+  if (g.n_exp > kMaxStreamExperts) return hipErrorInvalidValue;
   if (gated) hipLaunchKernelGGL(stream_gemm_kernel<true>, dim3(n_blocks), dim3(256), 0, st, g);
   else hipLaunchKernelGGL(stream_gemm_kernel<false>, dim3(n_blocks), dim3(256), 0, st, g);
   return hipGetLastError();

@@ -51,9 +51,6 @@ namespace {
 #ifndef MOE_TILE_XCD
 #define MOE_TILE_XCD 0
 #endif
-#ifndef MOE_TILE_MBW
-#define MOE_TILE_MBW 5
-#endif
 constexpr int MBW = MOE_TILE_MBW;           // 32-row MFMA blocks per wave (2 waves along M)
 constexpr int TBM = 64 * MBW, TBK = 32;
 constexpr int TBN = MOE_TILE_TBN, NSTAGE = MOE_TILE_NSTAGE;
