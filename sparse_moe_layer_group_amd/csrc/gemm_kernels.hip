@@ -193,11 +193,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs<TE> g) {
 // ============================================================================
 // Gated combine: y[t] = sum_s Y[TK + s*T + t] + sum_k gate[t][k] * Y[slot[t*K+k]]
 // (+ residual), float32 accumulation, shared experts first then k ascending
-// (the chosen ids ascend), one block per token, 16-byte vectors.
+// (the chosen ids ascend).  A 128-thread block covers 128 16-byte vectors of
+// one token row (grid: tokens x column blocks), so every thread issues all of
+// its K + S + 1 loads at once.
 // ============================================================================
 
+constexpr int COMBINE_THREADS = 128;
+
 template <typename TE>
-__global__ __launch_bounds__(256) void combine_kernel(const TE* __restrict__ Y,
+__global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const TE* __restrict__ Y,
                                                       const int32_t* __restrict__ slot,
                                                       const float* __restrict__ gate,
                                                       const TE* __restrict__ residual,
@@ -212,7 +216,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const TE* __restrict__ Y,
     g_s[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * CE; c < H; c += blockDim.x * CE) {
+  const int c = (blockIdx.y * COMBINE_THREADS + threadIdx.x) * CE;
+  if (c < H) {  // H % 128 == 0: whole vectors
     float acc[CE];
 #pragma unroll
     for (int q = 0; q < CE; ++q) acc[q] = 0.f;
@@ -267,8 +272,10 @@ int gemm_tile_m() { return 64; }
 template <typename TE>
 hipError_t launch_combine(const TE* Y, const int32_t* slot, const float* gate, const TE* residual,
                           TE* y, int T, int K, int H, int TK, int S, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel<TE>, dim3(T), dim3(256), 0, st, Y, slot, gate, residual, y, T,
-                     K, H, TK, S);
+  constexpr int CE = 16 / sizeof(TE);
+  const int ncb = (H / CE + COMBINE_THREADS - 1) / COMBINE_THREADS;
+  hipLaunchKernelGGL(combine_kernel<TE>, dim3(T, ncb), dim3(COMBINE_THREADS), 0, st, Y, slot, gate,
+                     residual, y, T, K, H, TK, S);
   return hipGetLastError();
 }
 

@@ -527,70 +527,122 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   }
 }
 
+// Exclusive prefix sums of v over the block's threads in thread order (all
+// threads call it; blockDim.x a multiple of 64, at most 1024).  Returns the
+// exclusive sum; *total receives the block total.
+MOE_DEV int block_exclusive_scan(int v, int* wave_tot /* LDS [16] */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int tw = wave_tot[w];
+    before += (w < wave) ? tw : 0;
+    all += tw;
+  }
+  __syncthreads();  // wave_tot may be reused by the next call
+  *total = all;
+  return before + inc - v;
+}
+
 // Work tables of the expert GEMMs over E routed experts then S shared experts
 // (T rows each), both with E+S+1 entries:
 //   chunk_start: prefix of ceil(rows/16) over experts with rows <= stream_max
 //                (served by the weight-streaming GEMM);
 //   mt_start:    prefix of ceil(rows/bm) over the other experts (tiled GEMM).
-__global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ hist, int nchunks,
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int nchunks,
                                                    int E, int S, int T, int K,
                                                    int32_t* __restrict__ base,
                                                    int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets, int stream_max,
                                                    int32_t* __restrict__ chunk_start, int bm,
                                                    int32_t* __restrict__ mt_start) {
-  __shared__ int sc[SEL_MAX_E + 2];
-  __shared__ int ta[SEL_MAX_E + 2];
-  __shared__ int tb[SEL_MAX_E + 2];
-  const int e = threadIdx.x;
+  __shared__ int wave_tot[16];
+  const int e = threadIdx.x;  // blockDim.x >= E + S + 1
   int cnt = 0;
   if (e < E)
     for (int c = 0; c < nchunks; ++c) cnt += hist[(size_t)c * E + e];
-  if (e < E) {
-    sc[e] = cnt;
-    const bool str = cnt <= stream_max;
-    ta[e] = str ? (cnt + 15) / 16 : 0;
-    tb[e] = str ? 0 : (cnt + bm - 1) / bm;
-  }
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0, aa = 0, ab = 0;
-    for (int i = 0; i < E; ++i) {
-      int v = sc[i];
-      sc[i] = acc;
-      acc += v;
-      int va = ta[i];
-      ta[i] = aa;
-      aa += va;
-      int vb = tb[i];
-      tb[i] = ab;
-      ab += vb;
-    }
-    sc[E] = acc;
-    const bool str = T <= stream_max;
-    for (int sh = 0; sh < S; ++sh) {
-      ta[E + sh] = aa;
-      aa += str ? (T + 15) / 16 : 0;
-      tb[E + sh] = ab;
-      ab += str ? 0 : (T + bm - 1) / bm;
-    }
-    ta[E + S] = aa;
-    tb[E + S] = ab;
-  }
-  __syncthreads();
+  // rows of entry e of the work tables: routed experts, then the shared ones
+  const int rows = e < E ? cnt : (e < E + S ? T : 0);
+  const bool str = rows <= stream_max;
+  int tot;
+  const int off = block_exclusive_scan(e < E ? cnt : 0, wave_tot, &tot);
+  const int sa = block_exclusive_scan(str ? (rows + 15) / 16 : 0, wave_tot, &tot);
+  const int sb = block_exclusive_scan(str ? 0 : (rows + bm - 1) / bm, wave_tot, &tot);
   if (e < E) {
     counts[e] = cnt;
-    offsets[e] = sc[e];
-    int run = sc[e];
+    offsets[e] = off;
+    int run = off;
     for (int c = 0; c < nchunks; ++c) {
       base[(size_t)c * E + e] = run;
       run += hist[(size_t)c * E + e];
     }
   }
-  if (e == 0) offsets[E] = sc[E];
-  for (int i = e; i <= E + S; i += blockDim.x) {
-    chunk_start[i] = ta[i];
-    mt_start[i] = tb[i];
+  if (e == E) offsets[E] = off;
+  if (e <= E + S) {
+    chunk_start[e] = sa;
+    mt_start[e] = sb;
+  }
+}
+
+// Small batches (at most PERM_SMALL_T tokens): hist, scan and scatter in one
+// workgroup, the chunk masks in LDS.
+constexpr int PERM_SMALL_T = 512;
+constexpr int PERM_SMALL_NC = PERM_SMALL_T / CHUNK;
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int T, int K, int E, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ slot,
+    int stream_max, int32_t* __restrict__ chunk_start, int bm, int32_t* __restrict__ mt_start) {
+  __shared__ unsigned long long m_s[PERM_SMALL_NC][SEL_MAX_E];
+  __shared__ int base_s[PERM_SMALL_NC][SEL_MAX_E];
+  __shared__ int wave_tot[16];
+  const int nc = (T + CHUNK - 1) / CHUNK;
+  for (int i = threadIdx.x; i < nc * E; i += blockDim.x) m_s[i / E][i % E] = 0ull;
+  __syncthreads();
+  for (int a = threadIdx.x; a < T * K; a += blockDim.x) {
+    const int t = a / K;
+    atomicOr(&m_s[t / CHUNK][idx[a]], 1ull << (t % CHUNK));
+  }
+  __syncthreads();
+  const int e = threadIdx.x;  // blockDim.x >= E + S + 1
+  int cnt = 0;
+  if (e < E)
+    for (int c = 0; c < nc; ++c) cnt += __popcll(m_s[c][e]);
+  const int rows = e < E ? cnt : (e < E + S ? T : 0);
+  const bool str = rows <= stream_max;
+  int tot;
+  const int off = block_exclusive_scan(e < E ? cnt : 0, wave_tot, &tot);
+  const int sa = block_exclusive_scan(str ? (rows + 15) / 16 : 0, wave_tot, &tot);
+  const int sb = block_exclusive_scan(str ? 0 : (rows + bm - 1) / bm, wave_tot, &tot);
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = off;
+    int run = off;
+    for (int c = 0; c < nc; ++c) {
+      base_s[c][e] = run;
+      run += __popcll(m_s[c][e]);
+    }
+  }
+  if (e == E) offsets[E] = off;
+  if (e <= E + S) {
+    chunk_start[e] = sa;
+    mt_start[e] = sb;
+  }
+  __syncthreads();
+  for (int a = threadIdx.x; a < T * K; a += blockDim.x) {
+    const int t = a / K, tl = t % CHUNK, c = t / CHUNK;
+    const int ex = idx[a];
+    const uint64_t below = (tl == 0) ? 0ull : (m_s[c][ex] & ((1ull << tl) - 1ull));
+    const int row = base_s[c][ex] + __popcll(below);
+    slot[a] = row;
+    perm[row] = t;
   }
 }
 
@@ -705,10 +757,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int K, int E, int S, uint64
                           int32_t* perm, int32_t* slot, int stream_max, int32_t* chunk_start,
                           int bm, int32_t* mt_start, hipStream_t st) {
   const int nc = perm_chunks(T);
+  if (T <= PERM_SMALL_T) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, T, K, E, S, counts,
+                       offsets, perm, slot, stream_max, chunk_start, bm, mt_start);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(hist_kernel, dim3(nc), dim3(256), 0, st, idx, T, K, E, masks, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(512), 0, st, hist, nc, E, S, T, K, base, counts,
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, hist, nc, E, S, T, K, base, counts,
                      offsets, stream_max, chunk_start, bm, mt_start);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
