@@ -689,6 +689,97 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, float* __
 // K chunks of the router: about H/8 each, a multiple of 128 (H % 128 == 0)
 static int router_chunk(int H) { return ((H + 7) / 8 + 127) / 128 * 128; }
 
+// Small batches: the bf16x3 router reading W_r (float32 [H][E]) directly.
+// Same tiling and K map as router_mfma_kernel; each lane loads the 8
+// consecutive k of its expert column as float32 (W_r stride E) and splits
+// them into the hi / mid / lo bfloat16 parts in registers, so no separate
+// split pass runs.
+__global__ __launch_bounds__(256) void router_fused_kernel(const bf16_t* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           float* __restrict__ P, int T, int H,
+                                                           int E, int kchunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 32;
+  const int e0 = blockIdx.y * 128 + wave * 32;
+  const int ks = blockIdx.z;
+  const int kb = ks * kchunk, ke = min(H, kb + kchunk);
+  if (e0 >= E) return;  // whole wave; no barrier in this kernel
+  const int koff = 32 * (lane >> 4);
+  const bf16_t* arow[2];
+  int ecol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + i * 16 + (lane & 15);
+    arow[i] = (t < T) ? x + (size_t)t * H + koff : nullptr;
+    ecol[i] = e0 + i * 16 + (lane & 15);
+  }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = kb; k < ke; k += 128) {
+    u32x4 a[2][4];
+    float w[2][4][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        a[i][q] = arow[i] ? *reinterpret_cast<const u32x4*>(arow[i] + k + q * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          w[j][q][r] = (ecol[j] < E) ? wr[(size_t)(k + koff + 8 * q + r) * E + ecol[j]] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 b[3][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          uint32_t pr[3][2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float v = w[j][q][2 * h + u];
+            const uint32_t hi = __float_as_uint(v) & 0xffff0000u;
+            const float r1 = v - __uint_as_float(hi);              // exact
+            const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
+            const float r2 = r1 - __uint_as_float(mid);            // exact, fits 8 bits
+            pr[0][u] = hi >> 16;
+            pr[1][u] = mid >> 16;
+            pr[2][u] = __float_as_uint(r2) >> 16;
+          }
+#pragma unroll
+          for (int pp = 0; pp < 3; ++pp) b[pp][j][h] = pr[pp][0] | (pr[pp][1] << 16);
+        }
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[i][q]), __builtin_bit_cast(bf16x8, b[pp][j]),
+                acc[i][j], 0, 0, 0);
+    }
+  }
+  float* Pk = P + (size_t)ks * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + i * 16 + 4 * (lane >> 4) + q;
+        const int e = e0 + j * 16 + (lane & 15);
+        if (t < T && e < E) Pk[(size_t)t * E + e] = acc[i][j][q];
+      }
+}
+
 int router_ksplit(int H) {
   const int chunk = router_chunk(H);
   return (H + chunk - 1) / chunk;
@@ -718,11 +809,19 @@ hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt
   const int ks = router_ksplit(H);
   const int chunk = router_chunk(H);
   if (x_bf16) {
+    const int tc = router_tile_chunks(T, H, E);
+#ifndef MOE_ROUTER_FUSED
+#define MOE_ROUTER_FUSED 1
+#endif
+    if (tc == 0 && MOE_ROUTER_FUSED) {
+      hipLaunchKernelGGL(router_fused_kernel, dim3((T + 31) / 32, (E + 127) / 128, ks), dim3(256),
+                         0, st, static_cast<const bf16_t*>(x), wr, P, T, H, E, chunk);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(router_split_kernel, dim3((H + 63) / 64, (E + 63) / 64), dim3(256), 0, st,
                        wr, wt3, H, E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int tc = router_tile_chunks(T, H, E);
     if (tc > 0) {
       const int nsteps = 3 * H / RT_TBK;
       const int spc = (nsteps + tc - 1) / tc;
