@@ -47,18 +47,34 @@ MOE_DEV float siluf(float v) { return v / (1.0f + expf(-v)); }
 
 // ---------------------------------------------------------------- wave helpers
 
-// (value, index) arg-max over the wave: larger value wins, equal values go to
-// the smaller index.  Every lane returns the winner.
-MOE_DEV void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off, kWave);
-    int oi = __shfl_xor(i, off, kWave);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
+MOE_DEV void argmax_take(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
   }
+}
+
+// one arg-max step with a DPP lane move (CTRL: a 16-lane-row pattern)
+template <int CTRL> MOE_DEV void argmax_dpp(float& v, int& i) {
+  const float ov =
+      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
+  argmax_take(v, i, ov, oi);
+}
+
+// (value, index) arg-max over the wave: larger value wins, equal values go to
+// the smaller index.  Every lane returns the winner.  The rule is associative
+// and commutative, so any reduction order gives the same winner: quad swaps
+// (lane ^ 1, lane ^ 2) and rotations by 4 and 8 within each 16-lane row use
+// DPP moves; the last two steps cross rows with lane shuffles.
+MOE_DEV void wave_argmax(float& v, int& i) {
+  argmax_dpp<0xb1>(v, i);   // quad_perm [1,0,3,2]
+  argmax_dpp<0x4e>(v, i);   // quad_perm [2,3,0,1]
+  argmax_dpp<0x124>(v, i);  // row_ror:4
+  argmax_dpp<0x128>(v, i);  // row_ror:8
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) argmax_take(v, i, __shfl_xor(v, off, kWave),
+                                                       __shfl_xor(i, off, kWave));
 }
 
 MOE_DEV float wave_sum(float v) {

@@ -401,10 +401,40 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ P
   }
   __syncthreads();
 
-  // group scores: lane g < G scans its group keeping the group_topn largest (descending)
+  // group scores: the sum of the group_topn largest z of each group
   float gscore = -INFINITY;
   int gidx = 0x7fffffff;
-  if (lane < G) {
+  const int lpg = gsz / epl;  // lanes per group when a lane's experts lie in one group
+  const bool par = group_topn <= 2 && gsz % epl == 0 && (lpg & (lpg - 1)) == 0 && lpg <= 32 &&
+                   G * lpg <= 64;
+  if (par) {
+    // each lane: the two largest of its experts, then merged across the
+    // group's lanes (xor steps stay inside an aligned power-of-two lane group)
+    float t1 = -INFINITY, t2 = -INFINITY;
+    for (int j = 0; j < epl; ++j) {
+      const int e = lane * epl + j;
+      const float v = (e < E) ? z[e] : -INFINITY;
+      if (v > t1) {
+        t2 = t1;
+        t1 = v;
+      } else if (v > t2) {
+        t2 = v;
+      }
+    }
+    for (int off = 1; off < lpg; off <<= 1) {
+      const float o1 = __shfl_xor(t1, off, kWave), o2 = __shfl_xor(t2, off, kWave);
+      const float hi = fmaxf(t1, o1);
+      t2 = (t1 >= o1) ? fmaxf(t2, o1) : fmaxf(t1, o2);
+      t1 = hi;
+    }
+    const float score = group_topn == 1 ? t1 : t1 + t2;
+    const float mine = __shfl(score, (lane < G ? lane : 0) * lpg, kWave);
+    if (lane < G) {
+      gscore = mine;
+      gidx = lane;
+    }
+  } else if (lane < G) {
+    // lane g < G scans its group keeping the group_topn largest (descending)
     float top[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     for (int i = 0; i < gsz; ++i) {
       float v = z[lane * gsz + i];
