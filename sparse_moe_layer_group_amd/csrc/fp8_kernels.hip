@@ -142,7 +142,8 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
   constexpr int CPS = ACPW + BCPW + 1;           // copies per wave per stage (+1: scales)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
 
-  const int n_nt = GATED ? g.N / (F8_TBN / 2) : g.N / F8_TBN;
+  // column tiles (N % 128 == 0; a down tile may be half past N)
+  const int n_nt = GATED ? g.N / (F8_TBN / 2) : (g.N + F8_TBN - 1) / F8_TBN;
   const int n_tasks = g.mt_start[g.n_exp] * n_nt;
   const int task = blockIdx.x;
   if (task >= n_tasks) return;  // uniform per workgroup, before any barrier
@@ -187,7 +188,9 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
 #pragma unroll
   for (int i = 0; i < BCPW; ++i) {
     const int r = 8 * (wave * BCPW + i) + (lane >> 3);
-    const int col = GATED ? nt * (F8_TBN / 2) + (r & (F8_TBN / 2 - 1)) : nt * F8_TBN + r;
+    // weight rows past N (a partial down tile) re-read row N-1; never stored
+    const int col =
+        GATED ? nt * (F8_TBN / 2) + (r & (F8_TBN / 2 - 1)) : min(nt * F8_TBN + r, g.N - 1);
     boff[i] = uint32_t(col) * uint32_t(K) + uint32_t(swz8(r, lane & 7) * 16);
   }
   const uint8_t* __restrict__ wsrc = (GATED && wave >= F8_NWAVE / 2) ? wb1 : wb0;
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
   // weight-block scales of this wave's columns: gate/up tiles use block nt of
   // s_gate and s_up; down tiles block (nt*256 + wn*64) / 128 of s_down
   const float* __restrict__ sw0 = g.ws0 + (size_t)e * NB * KB +
-                                  (size_t)(GATED ? nt : (nt * F8_TBN + wn * 64) / 128) * KB;
+                                  (size_t)(GATED ? nt : min((nt * F8_TBN + wn * 64) / 128, NB - 1)) * KB;
   const float* __restrict__ sw1 = GATED ? g.ws1 + (size_t)e * NB * KB + (size_t)nt * KB : sw0;
 
   // Held in registers before the pipeline starts (lane l: blocks l and 64 + l)
@@ -359,7 +362,8 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * 32 * F8_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (r < rows) g.out16[(size_t)(row_base + m0 + r) * g.N + col] = f32_to_bf16(acc[i][j][v]);
+          if (r < rows && col < g.N)
+            g.out16[(size_t)(row_base + m0 + r) * g.N + col] = f32_to_bf16(acc[i][j][v]);
         }
       }
     }
@@ -370,7 +374,7 @@ size_t tile_gemm_fp8_lds_bytes() { return size_t(F8_NSTAGE) * F8_STAGE; }
 
 template <bool GATED>
 static hipError_t launch_fp8_one(const TileArgs8& g, int max_mtiles, hipStream_t st) {
-  const int n_nt = GATED ? g.N / (F8_TBN / 2) : g.N / F8_TBN;
+  const int n_nt = GATED ? g.N / (F8_TBN / 2) : (g.N + F8_TBN - 1) / F8_TBN;
   const long long blocks = (long long)max_mtiles * n_nt;
   if (blocks <= 0) return hipSuccess;
   const size_t lds = tile_gemm_fp8_lds_bytes();

@@ -87,7 +87,8 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
   bf16_t* As = smem;                             // [NSTAGE][TBM][32]
   bf16_t* Bs = smem + NSTAGE * ASTAGE;           // [NSTAGE][TBN][32]
 
-  const int n_nt = GATED ? g.N / (TBN / 2) : g.N / TBN;
+  // column tiles (N % 128 == 0; a down tile may be half past N)
+  const int n_nt = GATED ? g.N / (TBN / 2) : (g.N + TBN - 1) / TBN;
   const int n_tasks = g.mt_start[g.n_exp] * n_nt;
 #if MOE_TILE_XCD
   // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
   for (int i = 0; i < BCPW; ++i) {
     const int r = 16 * (wave * BCPW + i) + (lane >> 2);
     const int chunk = swz(r, lane & 3);
-    const int col = GATED ? nt * (TBN / 2) + (r & (TBN / 2 - 1)) : nt * TBN + r;
+    // weight rows past N (a partial down tile) re-read row N-1; never stored
+    const int col = GATED ? nt * (TBN / 2) + (r & (TBN / 2 - 1)) : min(nt * TBN + r, g.N - 1);
     boff[i] = (uint32_t(col) * uint32_t(K) + uint32_t(chunk * 8)) * 2u;
   }
   // gate rows (0..TBN/2-1) are copied by the first half of the waves, up rows
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 32 * MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r < rows) {
+        if (r < rows && col < g.N) {
           const float val = GATED ? siluf(acc[i][j][v]) * acc[i][j + NJ / 2][v] : acc[i][j][v];
           g.out[(size_t)(row_base + m0 + r) * g.N + col] = f32_to_bf16(val);
         }
@@ -281,7 +283,7 @@ size_t tile_gemm_lds_bytes() { return size_t(NSTAGE) * (TBM + TBN) * TBK * sizeo
 
 template <bool GATED>
 static hipError_t launch_one(const TileArgs& g, int max_mtiles, hipStream_t st) {
-  const int n_nt = GATED ? g.N / (TBN / 2) : g.N / TBN;
+  const int n_nt = GATED ? g.N / (TBN / 2) : (g.N + TBN - 1) / TBN;
   // one workgroup per task, up to the largest task count the routing can
   // produce (workgroups past the actual count exit at once)
   long long blocks = (long long)max_mtiles * n_nt;

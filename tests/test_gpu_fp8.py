@@ -194,3 +194,15 @@ def test_v3_fp8_routing_and_sampled_output():
     del gi, y, out
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kw", [dict(T=300, hidden=1152, inter=384), dict(T=200, topk=1, n_shared=0)])
+def test_fp8_forward_shapes(kw):
+    c = S.get_config("mid_fp8").with_(**kw)
+    gi = GpuInputs(c)
+    y, out = gi.run_forward()
+    ref = _oracle(c, emulate=True)
+    check_routing(c, out, ref.routing, f"mid_fp8 {kw}")
+    emu = row_errors(y.float().cpu().numpy(), ref.y)
+    say(f"mid_fp8 {kw}: vs emulation max {emu.max():.3e} (median {np.median(emu):.3e})")
+    assert emu.max() <= EMU_TOL

@@ -152,3 +152,51 @@ def test_bias_update_bit_exact_and_skew_steps():
         ratios.append(O.load_ratio(out["counts"].cpu().numpy()))
     say(f"skew: max/mean load per step {np.round(ratios, 2).tolist()}")
     assert ratios[-1] < ratios[0]
+
+
+# --------------------------------------------------------------------------- routing shapes
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=300, group_topn=1),                                  # group score = largest z
+    dict(T=300, group_topn=3),                                  # top-3 sum (serial group scan)
+    dict(T=300, topk_groups=8),                                 # every group kept
+    dict(T=300, n_groups=1, topk_groups=1),                     # one group: plain top-K
+    dict(T=300, topk=1),
+    dict(T=257, n_experts=512, topk=8),                         # 8 experts per lane
+    dict(T=300, n_experts=160, topk=6),                         # 20-expert groups, 3 per lane
+    dict(T=2100, n_experts=64),                                 # tiled router, partial tiles
+    dict(T=2100, n_experts=512, bias_range=0.5),                # tiled router, large bias
+    dict(T=1, n_experts=32, n_groups=4, topk_groups=2, topk=4),
+])
+def test_routing_shapes(kw):
+    c = S.get_config("mid").with_(**kw)
+    cfg = moe.cfg_from(c)
+    x = S.gen_x(c, device=DEV)
+    wr = S.gen_router(c, DEV)
+    b = S.gen_bias(c, DEV)
+    out = moe.alloc_routing(cfg, c.T, DEV)
+    ws = moe.alloc_workspace(cfg, c.T, DEV)
+    moe.route(cfg, x, wr, b, out, ws)
+    torch.cuda.synchronize()
+    L, s, r, p = oracle_route(c, S.gen_x(c, device="cpu"), S.gen_bias(c, "cpu").numpy())
+    check_routing(c, out, r, f"routing {kw}")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=300, hidden=1152, inter=384),          # down output 4.5 column tiles of 256
+    dict(T=300, n_shared=0),
+    dict(T=200, topk=1),
+    dict(T=300, n_experts=160, topk=6),
+    dict(T=2100),                                 # tiled router, tiled GEMMs, 2+ row tiles
+])
+def test_forward_shapes(kw):
+    c = S.get_config("mid").with_(**kw)
+    say(f"forward shapes {kw}")
+    gi = GpuInputs(c)
+    y, out = gi.run_forward()
+    ref = _oracle_forward(c)
+    check_routing(c, out, ref.routing, f"forward {kw}")
+    err = row_errors(y.float().cpu().numpy(), ref.y)
+    say(f"forward {kw}: max row rel err {err.max():.3e}")
+    assert err.max() <= OUT_TOL["bf16"]
