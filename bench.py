@@ -128,7 +128,7 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "fp8"])
     ap.add_argument("--skew-steps", type=int, default=200,
                     help="skew workload: bias-update steps (forward timed at first, middle, last)")
-    ap.add_argument("--cpu-tokens", type=int, default=12,
+    ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens in the CPU oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run plain copies of known size (for HBM counter calibration) and exit")

@@ -13,9 +13,12 @@
 // saturated to +-448.  The encoder is integer arithmetic on the float32 bits,
 // so the codes do not depend on a hardware conversion mode.
 //
-// GEMM tile: F8_TBM token rows x 256 weight rows, one 128-wide K block per LDS
-// stage (128 bytes per row, eight 16-byte chunks stored at chunk ^ (row % 8)),
-// three stages filled by direct global->LDS copies two blocks ahead.  Eight
+// GEMM tile: F8_TBM (192) token rows x 256 weight rows, one 128-wide K block
+// per LDS stage (128 bytes per row, eight 16-byte chunks stored at
+// chunk ^ (row % 8)), two stages (116 KB) filled by direct global->LDS copies
+// one block ahead.  192 rows hold nearly every expert of a 4096-token batch
+// in one row tile, so its weights stream once (128-row tiles with three
+// stages measured 25% slower: second row tiles re-read the weights).  Eight
 // waves in 2 (rows) x 4 (columns).  Per K block and 32x32 output block: two
 // v_mfma_scale_f32_32x32x64_f8f6f4 (hardware block scales left at 1) into a
 // temporary, then acc += tmp * (row scale * weight-block scale).  The row
@@ -35,14 +38,14 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_F8_MBW
-#define MOE_F8_MBW 2
-#endif
 constexpr int F8_MBW = MOE_F8_MBW;          // 32-row MFMA blocks per wave
 constexpr int F8_TBM = 64 * F8_MBW;         // token rows per tile (2 waves along M)
 constexpr int F8_TBN = 256;                 // weight rows per tile
 constexpr int F8_TBK = 128;                 // K per stage (bytes per row) = one scale block
-constexpr int F8_NSTAGE = 3;
+#ifndef MOE_F8_NSTAGE
+#define MOE_F8_NSTAGE 2
+#endif
+constexpr int F8_NSTAGE = MOE_F8_NSTAGE;
 constexpr int F8_WN = 4;                    // waves along N
 constexpr int F8_NWAVE = 2 * F8_WN, F8_NTHREAD = 64 * F8_NWAVE;
 constexpr int F8_RPW = F8_TBM / F8_NWAVE;   // rows whose A scale one wave copies
@@ -52,6 +55,7 @@ constexpr int F8_SSTAGE = F8_NWAVE * 64 * 4;  // one 4-byte copy per lane per wa
 constexpr int F8_STAGE = F8_ASTAGE + F8_BSTAGE + F8_SSTAGE;
 static_assert(F8_TBM == kTileM8, "row tile shared with the tile prefix scan");
 static_assert(F8_RPW % 4 == 0 && F8_RPW <= 64, "scale copy layout");
+static_assert(F8_NSTAGE * F8_STAGE <= 160 * 1024, "LDS per workgroup");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -307,8 +311,9 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
-  static_assert(F8_MBW <= 3, "dispatch below covers up to 3 blocks");
+  static_assert(F8_MBW <= 4, "dispatch below covers up to 4 blocks");
   switch (mact) {
+    case 4: mainloop(std::integral_constant<int, (F8_MBW >= 4 ? 4 : 0)>{}); break;
     case 3: mainloop(std::integral_constant<int, (F8_MBW >= 3 ? 3 : 0)>{}); break;
     case 2: mainloop(std::integral_constant<int, 2>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
