@@ -40,13 +40,13 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> gemm_gate_up counters per launch
-    "decode": {"src_sha256": "42b576e62051a76ebe0cc65fba4a10f3592384f17a36cf38e74759a4ac3e25af",
-               "fetch_kib": 8099028.5, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "42b576e62051a76ebe0cc65fba4a10f3592384f17a36cf38e74759a4ac3e25af",
-                "fetch_kib": 12333410.7, "write_kib": 294912.3},
+    "decode": {"src_sha256": "4709ad78f470104197d7a133802d3726b11ed05c8f6c3d1fcd2b0be09fcc984c",
+               "fetch_kib": 8153487.2, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "4709ad78f470104197d7a133802d3726b11ed05c8f6c3d1fcd2b0be09fcc984c",
+                "fetch_kib": 12336734.0, "write_kib": 294912.6},
 }
 KERNEL_SOURCES = ("common.h", "kernels.h", "moe_api.cpp", "route_kernels.hip",
-                  "gemm_kernels.hip", "stream_gemm.hip", "tile_gemm.hip")
+                  "gemm_kernels.hip", "stream_gemm.hip", "tile_gemm.hip", "fp8_kernels.hip")
 
 
 def log(msg):
