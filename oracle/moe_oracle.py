@@ -13,7 +13,8 @@ and section:
   [V3]   "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token"
          (PaperTrace close reading of the DeepSeek-V3 technical report)
          §1.1 shapes; §1.3 sigmoid gating and node-limited routing (Eq 12,
-         13, 15); §1.4 auxiliary-loss-free balancing (Eq 16); §2.2 FP8
+         13, 15); §1.4 auxiliary-loss-free balancing (Eq 16) and the
+         sequence-wise balance loss (Eq 17-20); §2.2 FP8
          fine-grained quantisation; §5.1 deployment (shared expert as an
          always-selected expert).
   [DEP]  "DeepSeek-V3 复盘：MoE、MLA、FP8 与低成本叙事如何验算" (audit of the
@@ -35,6 +36,8 @@ Parity status of each function (what pins it in tests/test_oracle_*.py):
                         otherwise parity unpinned: the pages print no worked
                         example of the layer.
   bias_update           pinned (rule worked by hand from §1.4, golden file)
+  sequence_balance_loss pinned (closed forms for balanced and uniform
+                        affinities; sum f = E, sum P = 1; scalar-loop brute force)
   e4m3_* / quantize_1x128  pinned (all 256 codes; torch float8_e4m3fn)
 """
 from __future__ import annotations
@@ -347,6 +350,50 @@ def load_ratio(counts: np.ndarray) -> float:
     """Max over mean per-expert load."""
     c = np.asarray(counts, dtype=F64)
     return float(c.max() / c.mean())
+
+
+# ----------------------------------------------------------------------------
+# complementary sequence-wise balance loss ([V3] §1.4, Eq 17-20)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class BalanceLoss:
+    loss: np.ndarray   # [n_seq] float64: alpha * sum_i f_i P_i
+    f: np.ndarray      # [n_seq][E] float64: selection frequency, mean 1 over experts
+    P: np.ndarray      # [n_seq][E] float64: mean normalised affinity
+    gap: np.ndarray    # [T] float32: K-th minus (K+1)-th raw affinity of each token
+
+
+def sequence_balance_loss(s32: np.ndarray, topk: int, seq_len: int, alpha: float) -> BalanceLoss:
+    """The small sequence-wise balance loss V3 keeps beside the bias.
+
+    [V3] §1.4 (Eq 17-20): for each sequence of seq_len tokens,
+      f_i = E / (K * seq_len) * #{t : expert i is in the top-K of token t's
+            raw affinities s_t (the bias is not involved)},
+      P_i = mean over the sequence of s_{i,t} / sum_j s_{j,t},
+      loss = alpha * sum_i f_i * P_i.
+    Readings: the top-K is a plain top-K over all experts (no group limit)
+    with ties going to the lower index; sequences are consecutive blocks of
+    seq_len tokens.
+    """
+    s = np.asarray(s32, dtype=F32)
+    T, E = s.shape
+    assert T % seq_len == 0
+    order = np.argsort(-s.astype(F64), axis=1, kind="stable")   # descending, lower index first
+    top = order[:, :topk]
+    kth = np.take_along_axis(s, order[:, topk - 1:topk], axis=1)[:, 0]
+    nxt = (np.take_along_axis(s, order[:, topk:topk + 1], axis=1)[:, 0] if topk < E
+           else np.full(T, -np.inf, dtype=F32))
+    gap = (kth.astype(F64) - nxt.astype(F64)).astype(F32)
+    sel = np.zeros((T, E), dtype=np.int64)
+    np.put_along_axis(sel, top, 1, axis=1)
+    sn = s.astype(F64) / s.astype(F64).sum(axis=1, keepdims=True)
+    n_seq = T // seq_len
+    counts = sel.reshape(n_seq, seq_len, E).sum(axis=1)
+    f = counts.astype(F64) * E / (topk * seq_len)
+    P = sn.reshape(n_seq, seq_len, E).mean(axis=1)
+    loss = alpha * (f * P).sum(axis=1)
+    return BalanceLoss(loss=loss, f=f, P=P, gap=gap)
 
 
 # ----------------------------------------------------------------------------

@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 import oracle.moe_oracle as M
+from tests import test_oracle_balance as TB
 from tests import test_oracle_ffn as TF
 from tests import test_oracle_fp8 as T8
 from tests import test_oracle_routing as TR
@@ -20,7 +21,8 @@ def _patch(monkeypatch, name, fn):
 
 _orig = {n: getattr(M, n) for n in ("group_scores", "biased_scores", "gate_values", "permute",
                                      "expert_ffn", "bias_update", "router_affinity",
-                                     "e4m3_quantize", "select_experts")}
+                                     "e4m3_quantize", "select_experts",
+                                     "sequence_balance_loss")}
 
 
 def m_group_top1(z, n_groups, group_topn):
@@ -78,6 +80,25 @@ def m_select_ascending(s, b, n_groups, topk_groups, topk, group_topn=2):
     return _orig["select_experts"](-s, -b, n_groups, topk_groups, topk, group_topn)
 
 
+def m_bal_raw_P(s, K, seq_len, alpha):
+    r = _orig["sequence_balance_loss"](s, K, seq_len, alpha)
+    T, E = s.shape
+    P = np.asarray(s, np.float64).reshape(T // seq_len, seq_len, E).mean(axis=1)
+    return M.BalanceLoss(loss=alpha * (r.f * P).sum(axis=1), f=r.f, P=P, gap=r.gap)
+
+
+def m_bal_no_scale(s, K, seq_len, alpha):
+    r = _orig["sequence_balance_loss"](s, K, seq_len, alpha)
+    f = r.f * K / s.shape[1]
+    return M.BalanceLoss(loss=alpha * (f * r.P).sum(axis=1), f=f, P=r.P, gap=r.gap)
+
+
+def m_bal_smallest(s, K, seq_len, alpha):
+    r = _orig["sequence_balance_loss"](s, K, seq_len, alpha)
+    f = _orig["sequence_balance_loss"]((1 - np.asarray(s, np.float32)), K, seq_len, alpha).f
+    return M.BalanceLoss(loss=alpha * (f * r.P).sum(axis=1), f=f, P=r.P, gap=r.gap)
+
+
 CASES = [
     ("group_scores", m_group_top1, TR.test_selection_matches_subset_enumeration, (0,)),
     ("biased_scores", m_no_bias, TR.test_large_bias_forces_and_excludes_experts, ()),
@@ -90,6 +111,9 @@ CASES = [
     ("router_affinity", m_sigmoid_sign, TR.test_sigmoid_matches_scipy_expit, ()),
     ("e4m3_quantize", m_round_away, T8.test_midpoints_round_to_even_and_saturate, ()),
     ("select_experts", m_select_ascending, TR.test_plain_topk_when_all_groups_kept, ()),
+    ("sequence_balance_loss", m_bal_raw_P, TB.test_balanced_selection_gives_alpha, ()),
+    ("sequence_balance_loss", m_bal_no_scale, TB.test_balanced_selection_gives_alpha, ()),
+    ("sequence_balance_loss", m_bal_smallest, TB.test_concentrated_routing_is_penalised, ()),
 ]
 
 
