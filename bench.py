@@ -273,6 +273,7 @@ def main():
              "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kern.items() if n}}
 
     value = T / (ms_step / 1e3)
+    bal = balance_loss_timing(moe, torch, cfg, c, x, wr, ws, dev)
     cpu = None
     if args.cpu_tokens > 0:
         cpu = cpu_baseline(c, args.cpu_tokens, x, b)
@@ -298,9 +299,53 @@ def main():
         "roofline": roofline,
         "layer": layer,
         "cpu_baseline": cpu,
+        "balance_loss": bal,
         **({"skew": skew} if skew is not None else {}),
     }
     print(json.dumps(res), flush=True)
+
+
+def router_partials(T, H, E):
+    """Number of float32 [T][E] router partials the library's bf16 router writes:
+    K = 3H split into 128-aligned chunks of about H/8 for small batches; from
+    2048 tokens the tiled router (128 x 256 tiles, K steps of 32) uses about
+    256 workgroups' worth of chunks."""
+    chunk = ((H + 7) // 8 + 127) // 128 * 128
+    ks = (H + chunk - 1) // chunk
+    if T < 2048:
+        return ks
+    tiles = ((T + 127) // 128) * ((E + 255) // 256)
+    chunks = max(1, min(ks, 256 // tiles))
+    nsteps = 3 * H // 32
+    spc = (nsteps + chunks - 1) // chunks
+    return (nsteps + spc - 1) // spc
+
+
+def balance_loss_timing(moe, torch, cfg, c, x, wr, ws, dev, calls=5, alpha=1e-4):
+    """Sequence-wise balance loss over the batch as one sequence (router + loss
+    kernels), timed like the layer: HIP events per launch on the stream."""
+    T, E, K = c.T, c.n_experts, c.topk
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    moe.balance_loss(cfg, x, wr, T, alpha, loss, ws)
+    torch.cuda.synchronize()
+    moe.profile_read()
+    moe.profile_enable(True)
+    for _ in range(calls):
+        moe.balance_loss(cfg, x, wr, T, alpha, loss, ws)
+    torch.cuda.synchronize()
+    moe.profile_enable(False)
+    kern = moe.profile_read()
+    r_ms, r_n = kern["router_logits"]
+    b_ms, b_n = kern["balance_loss"]
+    b_s = b_ms / max(b_n, 1) / 1e3
+    # loss kernels: router partials read, s / sum(s) written and read back, top-K ids
+    ksplit = router_partials(T, c.hidden, E)
+    b_bytes = ksplit * T * E * 4 + 2 * T * E * 4 + 2 * T * K * 4
+    log(f"balance loss: router {r_ms / max(r_n, 1) * 1e3:.1f} us, loss kernels "
+        f"{b_s * 1e6:.1f} us per call; loss/alpha {float(loss[0]) / alpha:.4f}")
+    return {"seq_len": T, "alpha": alpha, "loss": float(loss[0]),
+            "router_us": round(r_ms / max(r_n, 1) * 1e3, 1), "loss_kernels_us": round(b_s * 1e6, 1),
+            "loss_kernels_gbs": round(b_bytes / b_s / 1e9, 1)}
 
 
 def cpu_baseline(c, n_tok, x_dev, b_dev):

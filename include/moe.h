@@ -15,6 +15,7 @@
  *   §1.3 (Eq 12)  output = shared experts' FFN + sum_k gate_k · FFN_{e_k};
  *   §1.4          loss-free bias step: b_e -= gamma if expert e's load is
  *                 above the mean, b_e += gamma if below, unchanged if equal;
+ *                 and the sequence-wise balance loss (Eq 17-20);
  *   §2.2          FP8 (E4M3) weights with one float32 scale per 128x128 block,
  *                 activations quantised online per 1x128 slice, float32
  *                 accumulation with the scales applied per 128-wide K block.
@@ -171,6 +172,26 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
  */
 int moe_bias_update(const moe_cfg* cfg, int64_t T, const int32_t* counts, float* bias,
                     float gamma, void* stream);
+
+/*
+ * Complementary sequence-wise balance loss of the router (page "02 ·
+ * DeepSeek-V3", §1.4, Eq 17-20), the small loss V3 keeps beside the bias.
+ * For each sequence (consecutive blocks of seq_len tokens, T % seq_len == 0):
+ *   f_e = E / (K * seq_len) * (tokens whose top-K of the raw affinities s,
+ *         without the bias and without the group limit, holds expert e;
+ *         ties go to the lower index),
+ *   P_e = mean over the sequence of s_e / sum_j s_j,
+ *   loss = alpha * sum_e f_e * P_e        (the pages use alpha = 1e-4).
+ *   x, w_router as in moe_route
+ *   loss device float [T/seq_len]
+ *   f, p device float [T/seq_len][E] each, or NULL
+ *   ws   workspace of at least moe_workspace_bytes(cfg, T) bytes
+ * Counts are exact; P and the loss are summed in float64 in a fixed order
+ * (deterministic).  T == 0 returns MOE_OK without reading pointers.
+ */
+int moe_balance_loss(const moe_cfg* cfg, int64_t T, int32_t seq_len, const void* x,
+                     const float* w_router, float alpha, float* loss, float* f, float* p,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Online activation quantisation to E4M3 (page "02 · DeepSeek-V3", §2.2: one

@@ -18,9 +18,8 @@ import torch
 
 __all__ = ["F32", "BF16", "E4M3", "MoeError", "lib", "lib_path", "make_cfg", "cfg_from",
            "workspace_bytes", "alloc_workspace", "alloc_routing", "route", "forward",
-           "bias_update", "quantize_1x128", "profile_enable", "profile_read", "status_string",
-           "abi_version",
-           "EXPORTED_SYMBOLS"]
+           "bias_update", "quantize_1x128", "balance_loss", "profile_enable", "profile_read",
+           "status_string", "abi_version", "EXPORTED_SYMBOLS"]
 
 F32, BF16, E4M3 = 0, 1, 2
 _DT_NAME = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
@@ -28,7 +27,8 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8}
 
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_bias_update",
                     "moe_profile_enable", "moe_profile_read", "moe_profile_kernel_name",
-                    "moe_status_string", "moe_abi_version", "moe_quantize_1x128")
+                    "moe_status_string", "moe_abi_version", "moe_quantize_1x128",
+                    "moe_balance_loss")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
         L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
                                        I32]
         L.moe_profile_read.restype = I32
+        L.moe_balance_loss.argtypes = [ctypes.POINTER(_Cfg), I64, ctypes.c_int32, P, P,
+                                       ctypes.c_float, P, P, P, P, SZ, P]
+        L.moe_balance_loss.restype = I32
         L.moe_quantize_1x128.argtypes = [P, I64, ctypes.c_int32, P, P, P]
         L.moe_quantize_1x128.restype = I32
         L.moe_profile_kernel_name.argtypes = [I32]
@@ -249,6 +252,26 @@ def forward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tens
                            ws.numel() if ws is not None else 0, _stream(stream))
     if rc != 0:
         raise MoeError(rc, "moe_forward")
+
+
+def balance_loss(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, seq_len: int, alpha: float,
+                 loss: torch.Tensor, ws: torch.Tensor, f: Optional[torch.Tensor] = None,
+                 p: Optional[torch.Tensor] = None, stream=None) -> None:
+    """moe_balance_loss: sequence-wise balance loss per sequence of seq_len tokens into ``loss``."""
+    T = x.shape[0]
+    H, E = cfg.hidden, cfg.n_experts
+    _check(x, "x", _TORCH_DT[cfg.act_dtype], (T, H))
+    _check(w_router, "w_router", torch.float32, (H, E))
+    n_seq = T // seq_len if seq_len > 0 else 0
+    _check(loss, "loss", torch.float32, (n_seq,))
+    for t, name in ((f, "f"), (p, "p")):
+        if t is not None:
+            _check(t, name, torch.float32, (n_seq, E))
+    rc = lib().moe_balance_loss(ctypes.byref(cfg), T, int(seq_len), _ptr(x), _ptr(w_router),
+                                ctypes.c_float(alpha), _ptr(loss), _ptr(f), _ptr(p), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_balance_loss")
 
 
 def quantize_1x128(x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #define MOE_DEV __device__ __forceinline__
 
 namespace moe {

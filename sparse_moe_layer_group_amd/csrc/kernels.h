@@ -109,4 +109,10 @@ struct TileArgs8 {
 constexpr int kTileM8 = 64 * MOE_F8_MBW;
 hipError_t launch_tile_gemm_fp8(const TileArgs8& g, bool gated, int max_mtiles, hipStream_t st);
 
+// ---- sequence-wise balance loss (balance_kernels.hip)
+int balance_chunks(int seq_len);  // token chunks per sequence in the reduction
+hipError_t launch_balance(const float* P, int ksplit, int T, int E, int K, int seq_len,
+                          float alpha, float* sn, int32_t* ids, double* psum, int32_t* pcnt,
+                          float* loss, float* f, float* p, hipStream_t st);
+
 }  // namespace moe

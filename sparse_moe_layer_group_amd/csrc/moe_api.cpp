@@ -22,6 +22,7 @@ struct Layout {
       mt_start;
   size_t hst, yst;
   size_t hs, xq, xs;  // E4M3 weights: H scales, quantised x and its scales
+  size_t bal_sn, bal_ids, bal_psum, bal_pcnt, bal_end;  // balance loss (after the routing part)
   size_t route_total, total;
 };
 
@@ -67,6 +68,19 @@ Layout make_layout(const moe_cfg& c, int64_t T) {
   }
   L.yst = take(rows * H * es);
   L.total = off;
+  // the balance loss reuses the space after the routing part
+  size_t b = L.route_total;
+  auto take_b = [&](size_t bytes) {
+    size_t o = b;
+    b += align_up(bytes);
+    return o;
+  };
+  L.bal_sn = take_b(size_t(T) * E * 4);
+  L.bal_ids = take_b(TK * 4);
+  L.bal_psum = take_b(size_t(T) * E * 8);  // at most T chunk rows of E partial sums
+  L.bal_pcnt = take_b(size_t(T) * E * 4);
+  L.bal_end = b;
+  L.total = std::max(L.total, L.bal_end);
   return L;
 }
 
@@ -119,11 +133,12 @@ int check_device() {
 // ---------------------------------------------------------------- instrumentation
 
 enum Slot {
-  K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_QUANT, K_NSLOTS
+  K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_QUANT, K_BAL,
+  K_NSLOTS
 };
-const char* const kSlotNames[K_NSLOTS] = {"router_logits", "select",  "permute",
-                                          "gemm_gate_up",  "gemm_down", "combine",
-                                          "bias_update",   "quantize"};
+const char* const kSlotNames[K_NSLOTS] = {"router_logits", "select",      "permute",
+                                          "gemm_gate_up",  "gemm_down",   "combine",
+                                          "bias_update",   "quantize",    "balance_loss"};
 
 struct Prof {
   bool on = false;
@@ -463,6 +478,34 @@ int moe_quantize_1x128(const void* x, int64_t rows, int32_t cols, uint8_t* q, fl
   hipStream_t st = static_cast<hipStream_t>(stream);
   MOE_TRY(timed(K_QUANT, st, [&] {
     return moe::launch_quant_1x128(static_cast<const bf16_t*>(x), rows, cols, q, scales, st);
+  }));
+  return MOE_OK;
+}
+
+int moe_balance_loss(const moe_cfg* cfg, int64_t T, int32_t seq_len, const void* x,
+                     const float* w_router, float alpha, float* loss, float* f, float* p, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if (seq_len <= 0 || T % seq_len != 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || loss == nullptr) return MOE_ERR_NULL;
+  const Layout L = make_layout(*cfg, T);
+  if (ws == nullptr || ws_bytes < L.bal_end) return MOE_ERR_WORKSPACE;
+  if ((rc = check_device()) != MOE_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = cfg->hidden, E = cfg->n_experts, Ti = int(T);
+  const bool xb = cfg->act_dtype == MOE_BF16;
+  float* P = at<float>(ws, L.P);
+  MOE_TRY(timed(K_ROUTER, st, [&] {
+    return moe::launch_router(x, xb, w_router, at<bf16_t>(ws, L.wt3), P, Ti, H, E, st);
+  }));
+  MOE_TRY(timed(K_BAL, st, [&] {
+    return moe::launch_balance(P, moe::router_partials(Ti, H, E, xb), Ti, E, cfg->topk, seq_len,
+                               alpha, at<float>(ws, L.bal_sn), at<int32_t>(ws, L.bal_ids),
+                               at<double>(ws, L.bal_psum), at<int32_t>(ws, L.bal_pcnt), loss, f,
+                               p, st);
   }));
   return MOE_OK;
 }

@@ -168,3 +168,20 @@ def test_quantize_argument_checks():
     assert L.moe_quantize_1x128(one, -1, 128, one, one, None) == -2
     assert L.moe_quantize_1x128(None, 0, 128, None, None, None) == 0    # no rows: nothing read
     assert L.moe_quantize_1x128(one, 4, 128, None, one, None) == -1
+
+
+def test_balance_loss_argument_checks():
+    L = moe.lib()
+    c = _v3()
+    one = ctypes.c_void_p(1)
+    big = ctypes.c_size_t(1 << 40)
+    assert L.moe_balance_loss(ctypes.byref(c), 100, 30, one, one, ctypes.c_float(1e-4), one, None,
+                              None, one, big, None) == -2          # T % seq_len != 0
+    assert L.moe_balance_loss(ctypes.byref(c), 100, 0, one, one, ctypes.c_float(1e-4), one, None,
+                              None, one, big, None) == -2
+    assert L.moe_balance_loss(ctypes.byref(c), 100, 50, one, one, ctypes.c_float(1e-4), None, None,
+                              None, one, big, None) == -1          # loss output missing
+    assert L.moe_balance_loss(ctypes.byref(c), 100, 50, one, one, ctypes.c_float(1e-4), one, None,
+                              None, one, ctypes.c_size_t(100), None) == -4
+    assert L.moe_balance_loss(ctypes.byref(c), 0, 1, None, None, ctypes.c_float(1e-4), None, None,
+                              None, None, ctypes.c_size_t(0), None) == 0
