@@ -87,4 +87,23 @@ MOE_DEV float wave_sum(float v) {
 
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// ---------------------------------------------------------------- global -> LDS copies
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over [base, base + bytes) for raw loads (stride 0; dword 3
+// selects the 32-bit data format).  Loads past `bytes` return zeros.
+MOE_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from byte offset voff of the buffer straight into LDS:
+// lane l writes dst + 16 l (dst uniform).  The buffer form (MUBUF) is used
+// rather than global_load_lds: this compiler treats the FLAT-encoded copy as
+// a possible LDS access and then makes every later LDS-read wait drain the
+// whole LDS queue (lgkmcnt(0)), serialising fragment reads with the MFMAs.
+MOE_DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff, bf16_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
 }  // namespace moe

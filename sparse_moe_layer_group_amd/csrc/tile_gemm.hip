@@ -3,31 +3,39 @@
 // Method: "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token", §1.1 (SwiGLU
 // experts) and §1.3 Eq 12.
 //
-// Workgroup tile: 256 rows x 256 weight rows, K in steps of 64.  Gate/up
-// tiles hold 128 columns: weight rows 0..127 come from W_gate and 128..255
-// from W_up for the same columns, so SiLU(gate) * up is formed in registers.
-// Down tiles hold 256 columns of W_down.  Eight waves in 2 (rows) x 4
-// (columns), each owning a 128 x 64 sub-tile as 4 x 2 v_mfma_f32_32x32x16_bf16
-// blocks (128 fp32 accumulators per lane), two waves per SIMD so one
-// multiplies while the other waits.  32-row blocks past the expert's row count
-// are skipped per wave.
+// Workgroup tile: kTileM (320) rows x 256 weight rows, K in steps of 32.
+// Gate/up tiles hold 128 columns: weight rows 0..127 come from W_gate and
+// 128..255 from W_up for the same columns, so SiLU(gate) * up is formed in
+// registers.  Down tiles hold 256 columns of W_down.  Eight waves in 2 (rows)
+// x 4 (columns), each owning a 160 x 64 sub-tile as 5 x 2
+// v_mfma_f32_32x32x16_bf16 blocks, two waves per SIMD.  32-row blocks past
+// the expert's row count are skipped per wave.
 //
-// LDS: four stages of A[256][32] and B[256][32] bf16 (32 KB each).  A row is
-// four 16-byte chunks; chunk c of row r is stored at position c ^ ((r/2) & 3),
-// so the eight rows read together by a fragment load hit distinct banks.
-// Global memory is copied straight into LDS (global_load_lds, 1 KB per wave
-// instruction, no registers), three K steps ahead of the step being
-// multiplied.  Each step waits for its own copies with an explicit vmcnt
-// (the copies of the next two steps stay in flight), meets the workgroup at
-// one barrier, refills the stage freed by the previous step and multiplies.
-// Copies past the last step re-read the last step so that every step issues
-// the same number of copies.
+// Copies.  Global memory is copied straight into LDS (buffer_load ... lds,
+// 1 KB per wave instruction, no registers).  A wave's copies complete in
+// issue order, so the roles are split: waves 0-3 copy only weight rows into a
+// ring of NSB stages and waves 4-7 only token rows into a ring of NSA stages,
+// each NS-2 steps ahead of use, and each group waits only for its own copies.
+// (Deeper weight rings, NSB = 5 or 6 with NSA = 3, measured slower than
+// NSA = NSB = 4 at 8192 tokens.)  A row is four 16-byte chunks; chunk c of row
+// r sits at position c ^ ((r/2) & 3).
+//
+// Schedule of K step kt (two k16 slices s0, s1):
+//   MFMAs of s0 of kt, with the s1 fragment reads of kt interleaved
+//   wait for this wave's copies of kt+1; workgroup barrier
+//   issue the copies of the step that reuses the stages of kt-1
+//   MFMAs of s1 of kt, with the s0 fragment reads of kt+1 interleaved
+// Every fragment read is issued among MFMAs that do not need it (one read
+// after each MFMA), and the barrier falls between two MFMA groups instead of
+// in front of the reads; scheduling-group barriers fix this order for the
+// compiler.  Copies past the last step re-read the last step so that every
+// step issues the same number of copies.
 //
 // Task order: for each expert and column tile, its row tiles are consecutive
 // workgroups, so the workgroups sharing a weight tile run together and read it
 // from HBM once (L2 / MALL serve the others).  Dealing each XCD a contiguous
 // eighth of the tasks (MOE_TILE_XCD=1) keeps an expert's token rows in one L2
-// and cuts L2 misses, but measured 6% slower at 8192 tokens.
+// but measured no faster.
 #include <type_traits>
 
 #include "common.h"
@@ -37,30 +45,28 @@ namespace moe {
 
 namespace {
 
-// Tile configuration: TBN weight rows per workgroup tile (128: two workgroups
-// per CU; 256: one), NSTAGE LDS stages (copies run NSTAGE-1 steps ahead).
-#ifndef MOE_TILE_TBN
-#define MOE_TILE_TBN 256
-#endif
-#ifndef MOE_TILE_NSTAGE
-#define MOE_TILE_NSTAGE 4
-#endif
-#ifndef MOE_TILE_WN
-#define MOE_TILE_WN 4
-#endif
 #ifndef MOE_TILE_XCD
 #define MOE_TILE_XCD 0
 #endif
-constexpr int MBW = MOE_TILE_MBW;           // 32-row MFMA blocks per wave (2 waves along M)
-constexpr int TBM = 64 * MBW, TBK = 32;
-constexpr int TBN = MOE_TILE_TBN, NSTAGE = MOE_TILE_NSTAGE;
-constexpr int WN = MOE_TILE_WN;            // waves along N (2 along M)
-constexpr int NWAVE = 2 * WN, NTHREAD = 64 * NWAVE;
-constexpr int WGS_PER_CU = (TBN == 128 && WN == 2) ? 2 : 1;
-constexpr int ASTAGE = TBM * TBK;  // bf16 elements of A per stage
+#ifndef MOE_TILE_NSA
+#define MOE_TILE_NSA 4
+#endif
+#ifndef MOE_TILE_NSB
+#define MOE_TILE_NSB 4
+#endif
+constexpr int MBW = MOE_TILE_MBW;            // 32-row MFMA blocks per wave (2 waves along M)
+constexpr int TBM = 64 * MBW, TBN = 256, TBK = 32;
+constexpr int NSA = MOE_TILE_NSA, NSB = MOE_TILE_NSB;
+constexpr int WN = 4, NWAVE = 2 * WN, NTHREAD = 64 * NWAVE;
+constexpr int NJ = TBN / WN / 32;            // 32-column MFMA blocks per wave
+constexpr int ASTAGE = TBM * TBK, BSTAGE = TBN * TBK;  // bf16 elements per stage
+constexpr int ACP = TBM / 16 / 4;            // 1 KB copies per token-row wave per step
+constexpr int BCP = TBN / 16 / 4;            // ... per weight-row wave
 static_assert(TBM == kTileM, "row tile shared with the tile prefix scan");
-
-typedef __attribute__((address_space(3))) void lds_void;
+static_assert(TBM % 64 == 0 && NJ == 2, "tile configuration");
+static_assert(NSA >= 3 && NSB >= 3, "copies run at least one step ahead of the barrier");
+static_assert((NSA * ASTAGE + NSB * BSTAGE) * 2 <= 160 * 1024, "LDS per CU");
+static_assert(NSA * ACP < 64 && NSB * BCP < 64, "vmcnt field is 6 bits");
 
 MOE_DEV int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 
@@ -68,33 +74,29 @@ MOE_DEV bf16x8 ld_frag(const bf16_t* base, int row, int chunk) {
   return *reinterpret_cast<const bf16x8*>(base + row * TBK + (swz(row, chunk) << 3));
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4 and lgkmcnt 11:8 left at their maxima (no wait)
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
+
 }  // namespace
 
-// Wave tile 128 x TBN/WN.  (The tile configuration is a set of namespace
-// constants rather than template parameters: with more than one template
-// parameter this compiler does not emit the host-side launch stubs.)
+// (The tile configuration is a set of namespace constants rather than
+// template parameters: with more than one template parameter this compiler
+// does not emit the host-side launch stubs.)
 template <bool GATED>
-__global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs g) {
-  constexpr int BSTAGE = TBN * TBK;              // bf16 elements of B per stage
-  constexpr int AGRP = TBM / 16;                 // 16-row groups of A per stage
-  constexpr int ACPW = (AGRP + NWAVE - 1) / NWAVE;  // 1 KB copies of A per wave (at most)
-  constexpr int ACPW_MIN = AGRP / NWAVE;         // ... at least
-  constexpr int BCPW = TBN / 16 / NWAVE;         // 1 KB copies of B per wave per step
-  constexpr int NJ = TBN / WN / 32;              // 32-column MFMA blocks per wave
-  static_assert(ACPW_MIN >= 1 && BCPW >= 1 && NJ >= 2 && NJ % 2 == 0, "tile configuration");
-  constexpr int CPS = ACPW_MIN + BCPW;           // copies per wave per step (smallest)
+__global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  bf16_t* As = smem;                             // [NSTAGE][TBM][32]
-  bf16_t* Bs = smem + NSTAGE * ASTAGE;           // [NSTAGE][TBN][32]
+  bf16_t* As = smem;                  // [NSA][TBM][32]
+  bf16_t* Bs = smem + NSA * ASTAGE;   // [NSB][TBN][32]
 
   // column tiles (N % 128 == 0; a down tile may be half past N)
   const int n_nt = GATED ? g.N / (TBN / 2) : (g.N + TBN - 1) / TBN;
   const int n_tasks = g.mt_start[g.n_exp] * n_nt;
 #if MOE_TILE_XCD
   // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-  // b % 8).  XCD x takes the x-th contiguous eighth of the actual task list,
-  // so the column tiles of one expert run on one XCD and its token rows are
-  // fetched into one L2.
+  // b % 8).  XCD x takes the x-th contiguous eighth of the task list, so the
+  // column tiles of one expert run in one XCD and its token rows are fetched
+  // into one L2.
   const int per = (n_tasks + 7) >> 3;
   const int j = blockIdx.x >> 3;
   const int task = (blockIdx.x & 7) * per + j;
@@ -123,42 +125,66 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
   const int K = g.K;
   const int nk = K / TBK;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const bool copies_b = wave < 4;       // weight-row copier, else token-row copier
+  const int cw = wave & 3;              // index within the copier group
 
-  // ---- copy sources.  Copy i of wave w fills 16 rows of a stage (A row group
-  // w + NWAVE i, B rows 16(w*BCPW + i)..); lane l writes LDS bytes 16 l of that
-  // 1 KB, i.e. row r0 + l/4 at swizzled position l%4, which holds logical chunk
-  // swz(row, l%4).  32-bit byte offsets from uniform base pointers.
-  // (A offsets stay below T * K * 2 bytes: x rows are token ids < T; staged
-  // rows are addressed from the expert's first row)
-  uint32_t aoff[ACPW], boff[BCPW];
-  const char* __restrict__ abase =
-      reinterpret_cast<const char*>(GATED ? g.a : g.a + (size_t)row_base * K);
-  const char* __restrict__ wb0 = reinterpret_cast<const char*>(g.w0 + (size_t)e * g.N * K);
-  const char* __restrict__ wb1 =
-      GATED ? reinterpret_cast<const char*>(g.w1 + (size_t)e * g.N * K) : wb0;
+  // ---- copy sources.  Copy i of a weight-row wave fills B rows
+  // 16 (BCP cw + i) .. +15; copy i of a token-row wave fills A rows
+  // 16 (ACP cw + i) .. +15.  Lane l writes LDS bytes 16 l of the 1 KB, i.e.
+  // row r0 + l/4 at swizzled position l%4, which holds logical chunk
+  // swz(row, l%4).  Byte offsets into buffer resources: x [T][K] (gate/up) or
+  // the staged rows from the expert's first one (down), and the expert's
+  // weight matrices [N][K]; x rows are token ids < T.
+  uint32_t off[ACP > BCP ? ACP : BCP];
+  __amdgpu_buffer_rsrc_t crs;
+  if (copies_b) {
+    const uint32_t wbytes = uint32_t(g.N) * uint32_t(K) * 2u;
+    // gate rows (0..127) are copied by waves 0-1, up rows by waves 2-3
+    const bf16_t* w = (GATED && cw >= 2) ? g.w1 : g.w0;
+    crs = buffer_rsrc(w + (size_t)e * g.N * K, wbytes);
 #pragma unroll
-  for (int i = 0; i < ACPW; ++i) {
-    const int r = 16 * min(wave + NWAVE * i, AGRP - 1) + (lane >> 2);
-    const int chunk = swz(r, lane & 3);
-    const int m = m0 + min(r, rows - 1);  // rows past the count re-read a valid row
-    int arow;
-    if (GATED) arow = shared ? m : g.perm[row_base + m];
-    else arow = m;
-    aoff[i] = (uint32_t(arow) * uint32_t(K) + uint32_t(chunk * 8)) * 2u;
-  }
+    for (int i = 0; i < BCP; ++i) {
+      const int r = 16 * (BCP * cw + i) + (lane >> 2);
+      // weight rows past N (a partial down tile) re-read row N-1; never stored
+      const int col = GATED ? nt * (TBN / 2) + (r & (TBN / 2 - 1)) : min(nt * TBN + r, g.N - 1);
+      off[i] = (uint32_t(col) * uint32_t(K) + uint32_t(swz(r, lane & 3) * 8)) * 2u;
+    }
+  } else {
+    const int staged_rows = g.TK + (g.n_exp - g.E) * g.T;
+    crs = GATED ? buffer_rsrc(g.a, uint32_t(g.T) * uint32_t(K) * 2u)
+                : buffer_rsrc(g.a + (size_t)row_base * K,
+                              uint32_t(staged_rows - row_base) * uint32_t(K) * 2u);
 #pragma unroll
-  for (int i = 0; i < BCPW; ++i) {
-    const int r = 16 * (wave * BCPW + i) + (lane >> 2);
-    const int chunk = swz(r, lane & 3);
-    // weight rows past N (a partial down tile) re-read row N-1; never stored
-    const int col = GATED ? nt * (TBN / 2) + (r & (TBN / 2 - 1)) : min(nt * TBN + r, g.N - 1);
-    boff[i] = (uint32_t(col) * uint32_t(K) + uint32_t(chunk * 8)) * 2u;
+    for (int i = 0; i < ACP; ++i) {
+      const int r = 16 * (ACP * cw + i) + (lane >> 2);
+      const int m = m0 + min(r, rows - 1);  // rows past the count re-read a valid row
+      const int arow = GATED ? (shared ? m : g.perm[row_base + m]) : m;
+      off[i] = (uint32_t(arow) * uint32_t(K) + uint32_t(swz(r, lane & 3) * 8)) * 2u;
+    }
   }
-  // gate rows (0..TBN/2-1) are copied by the first half of the waves, up rows
-  // by the second half
-  const char* __restrict__ wsrc = (GATED && wave >= NWAVE / 2) ? wb1 : wb0;
+
+  // copies of K step kt (steps past the end re-read the last step)
+  auto copy_step = [&](int kt) {
+    const uint32_t koff = uint32_t(min(kt, nk - 1) * TBK * 2);
+    if (copies_b) {
+      bf16_t* d = Bs + (kt % NSB) * BSTAGE + 16 * BCP * cw * TBK;
+#pragma unroll
+      for (int i = 0; i < BCP; ++i) copy16_to_lds(crs, off[i] + koff, d + 16 * i * TBK);
+    } else {
+      bf16_t* d = As + (kt % NSA) * ASTAGE + 16 * ACP * cw * TBK;
+#pragma unroll
+      for (int i = 0; i < ACP; ++i) copy16_to_lds(crs, off[i] + koff, d + 16 * i * TBK);
+    }
+  };
+  // wait until this wave's copies of all but its last n issued steps landed
+  auto wait_copies = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm(n * BCP));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(n * ACP));
+  };
 
   // ---- wave sub-tile: active 32-row blocks (uniform per wave)
   const int mrows = rows - wm * 32 * MBW;
@@ -173,85 +199,77 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // B sub-tile rows of this wave in the staged tile: gated waves take the same
-  // columns of gate (first half of their blocks) and up (second half)
+  // columns of gate (block 0) and up (block 1)
   int brow0[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-    brow0[j] = GATED ? ((j < NJ / 2) ? (wn * (TBN / 2 / WN) + 32 * j)
-                                     : (TBN / 2 + wn * (TBN / 2 / WN) + 32 * (j - NJ / 2)))
-                     : (wn * (TBN / WN) + 32 * j);
+    brow0[j] = GATED ? (j * (TBN / 2) + wn * (TBN / 2 / WN)) : (wn * (TBN / WN) + 32 * j);
   const int arow0 = wm * 32 * MBW + (lane & 31);
 
-  // copies of K step kt into LDS stage kt % NSTAGE (steps past the end re-read
-  // the last step)
-  auto copy_step = [&](int kt) {
-    const uint32_t koff = uint32_t(min(kt, nk - 1) * TBK * 2);
-    const int stage = kt % NSTAGE;
-    bf16_t* a = As + stage * ASTAGE + (16 * wave) * TBK;
-    bf16_t* b = Bs + stage * BSTAGE + (16 * BCPW * wave) * TBK;
-#pragma unroll
-    for (int i = 0; i < ACPW; ++i)
-      if (i < ACPW_MIN || wave + NWAVE * i < AGRP)  // uniform per wave
-        __builtin_amdgcn_global_load_lds(abase + (aoff[i] + koff),
-                                         (lds_void*)(a + 16 * NWAVE * i * TBK), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BCPW; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc + (boff[i] + koff), (lds_void*)(b + 16 * i * TBK), 16,
-                                       0, 0);
-  };
-  // MACT active 32-row blocks: fragments of k16 slice s+1 are read while the
-  // MFMAs of slice s run; straight-line code for each MACT
-  auto compute = [&](int stage, auto mact_c) {
+  auto mainloop = [&](auto mact_c) {
     constexpr int MACT = decltype(mact_c)::value;
-    const bf16_t* a = As + stage * ASTAGE;
-    const bf16_t* b = Bs + stage * BSTAGE;
-    bf16x8 af[2][MBW], bf[2][NJ];
-    auto rd = [&](int s, bf16x8 (&afr)[MBW], bf16x8 (&bfr)[NJ]) {
+    struct Frags { bf16x8 a[MBW], b[NJ]; };
+    auto rd = [&](Frags& f, int kt, int s) {
+      const bf16_t* a = As + (kt % NSA) * ASTAGE;
+      const bf16_t* b = Bs + (kt % NSB) * BSTAGE;
       const int ch = 2 * s + (lane >> 5);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = ld_frag(b, brow0[j] + (lane & 31), ch);
+      for (int j = 0; j < NJ; ++j) f.b[j] = ld_frag(b, brow0[j] + (lane & 31), ch);
 #pragma unroll
-      for (int i = 0; i < MACT; ++i) afr[i] = ld_frag(a, arow0 + 32 * i, ch);
+      for (int i = 0; i < MACT; ++i) f.a[i] = ld_frag(a, arow0 + 32 * i, ch);
     };
-    rd(0, af[0], bf[0]);
-#pragma unroll
-    for (int s = 0; s < TBK / 16; ++s) {
-      if (s + 1 < TBK / 16) rd(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+    auto mma = [&](const Frags& f) {
 #pragma unroll
       for (int i = 0; i < MACT; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j],
-                                                             acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // ---- pipeline: copies run NSTAGE-1 steps ahead.  At step kt a wave waits
-  // until its copies of step kt have landed (2 * CPW copies per step; the
-  // copies of steps kt+1 .. kt+NSTAGE-2 stay in flight), the workgroup meets
-  // (every wave's copies of step kt are in LDS, and every wave has finished
-  // multiplying step kt-1), the stage of step kt-1 is refilled with step
-  // kt+NSTAGE-1, and step kt is multiplied.
-  // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
-  // 6:4 and lgkmcnt 11:8 left at their maxima (no wait)
-  constexpr int VMWAIT = (NSTAGE - 2) * CPS;
-  static_assert(VMWAIT < 64, "vmcnt field is 6 bits");
-  constexpr int WAITIMM = (VMWAIT & 15) | ((VMWAIT >> 4) << 14) | 0x70 | 0xf00;
-  auto mainloop = [&](auto mact_c) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    const int lead = copies_b ? NSB - 1 : NSA - 1;  // steps a wave's copies run ahead
+    for (int p = 0; p < lead; ++p) copy_step(p);
+    // this wave's step 0 landed: its copies of steps 1 .. lead-1 stay in flight
+    if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSB - 2) * BCP));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSA - 2) * ACP));
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    rd(f0, 0, 0);
+    // instruction order inside a phase: one fragment read after each of the
+    // first MACT+2 MFMAs, then the remaining MFMAs
+    auto interleave = [&]() {
 #pragma unroll
-    for (int p = 0; p < NSTAGE - 1; ++p) copy_step(p);
+      for (int k = 0; k < MACT + NJ; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      if (MACT * NJ > MACT + NJ) __builtin_amdgcn_sched_group_barrier(0x008, MACT * NJ - MACT - NJ, 0);
+    };
     for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(WAITIMM);  // this wave's copies of step kt are done
+      rd(f1, kt, 1);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // this wave's copies of kt+1 landed; after the barrier every wave's
+      // have, and every wave has read its fragments of step kt-1, so the
+      // stages of kt-1 are refilled with step kt-1+NSB (weights) or
+      // kt-1+NSA (token rows).  After the last step the reads of step nk
+      // fetch data that is never used.
+      if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSB - 3) * BCP));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSA - 3) * ACP));
       __builtin_amdgcn_s_barrier();
-      copy_step(kt + NSTAGE - 1);
-      compute(kt % NSTAGE, mact_c);
+      copy_step(kt + lead);
+      __builtin_amdgcn_sched_barrier(0);
+      rd(f0, kt + 1, 0);
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): no copy left in flight
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no copy left in flight
   };
+  (void)wait_copies;
   static_assert(MBW <= 5, "dispatch below covers up to 5 blocks");
   switch (mact) {
     case 5: mainloop(std::integral_constant<int, (MBW >= 5 ? 5 : 0)>{}); break;
-    case 4: mainloop(std::integral_constant<int, 4>{}); break;
+    case 4: mainloop(std::integral_constant<int, (MBW >= 4 ? 4 : 0)>{}); break;
     case 3: mainloop(std::integral_constant<int, 3>{}); break;
     case 2: mainloop(std::integral_constant<int, 2>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
@@ -262,7 +280,7 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
   // column l%32
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
-    if (i >= mact) break;
+    if (i >= mact) continue;  // uniform; keeps the loop unrolled
 #pragma unroll
     for (int j = 0; j < (GATED ? NJ / 2 : NJ); ++j) {
       const int col = GATED ? (nt * (TBN / 2) + wn * (TBN / 2 / WN) + 32 * j + (lane & 31))
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(NTHREAD, WGS_PER_CU) void tile_gemm_kernel(TileArgs
   }
 }
 
-size_t tile_gemm_lds_bytes() { return size_t(NSTAGE) * (TBM + TBN) * TBK * sizeof(bf16_t); }
+size_t tile_gemm_lds_bytes() { return size_t(NSA * ASTAGE + NSB * BSTAGE) * sizeof(bf16_t); }
 
 template <bool GATED>
 static hipError_t launch_one(const TileArgs& g, int max_mtiles, hipStream_t st) {
