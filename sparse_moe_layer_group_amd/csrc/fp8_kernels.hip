@@ -13,22 +13,7 @@
 // saturated to +-448.  The encoder is integer arithmetic on the float32 bits,
 // so the codes do not depend on a hardware conversion mode.
 //
-// GEMM tile: F8_TBM (192) token rows x 256 weight rows, one 128-wide K block
-// per LDS stage (128 bytes per row, eight 16-byte chunks stored at
-// chunk ^ (row % 8)), two stages (116 KB) filled by direct global->LDS copies
-// one block ahead.  192 rows hold nearly every expert of a 4096-token batch
-// in one row tile, so its weights stream once (128-row tiles with three
-// stages measured 25% slower: second row tiles re-read the weights).  Eight
-// waves in 2 (rows) x 4 (columns).  Per K block and 32x32 output block: two
-// v_mfma_scale_f32_32x32x64_f8f6f4 (hardware block scales left at 1) into a
-// temporary, then acc += tmp * (row scale * weight-block scale).  The row
-// scales of the block ride along with the A copies into LDS; a wave's
-// weight-block scales (one per K block) are loaded into registers before the
-// pipeline starts.
-// Gate/up tiles hold 128 columns of W_gate and the same 128 of W_up, which is
-// exactly one 1x128 slice of the SwiGLU output H: the epilogue forms
-// SiLU(gate) * up, reduces each row's max-abs across the four column waves
-// through LDS, and writes H as E4M3 codes plus one scale per row.
+// GEMM: see the comment above tile_gemm_fp8_kernel.
 #include <type_traits>
 
 #include "common.h"
@@ -37,39 +22,6 @@
 namespace moe {
 
 namespace {
-
-constexpr int F8_MBW = MOE_F8_MBW;          // 32-row MFMA blocks per wave
-constexpr int F8_TBM = 64 * F8_MBW;         // token rows per tile (2 waves along M)
-constexpr int F8_TBN = 256;                 // weight rows per tile
-constexpr int F8_TBK = 128;                 // K per stage (bytes per row) = one scale block
-#ifndef MOE_F8_NSTAGE
-#define MOE_F8_NSTAGE 2
-#endif
-constexpr int F8_NSTAGE = MOE_F8_NSTAGE;
-constexpr int F8_WN = 4;                    // waves along N
-constexpr int F8_NWAVE = 2 * F8_WN, F8_NTHREAD = 64 * F8_NWAVE;
-constexpr int F8_RPW = F8_TBM / F8_NWAVE;   // rows whose A scale one wave copies
-constexpr int F8_ASTAGE = F8_TBM * F8_TBK;  // bytes
-constexpr int F8_BSTAGE = F8_TBN * F8_TBK;
-constexpr int F8_SSTAGE = F8_NWAVE * 64 * 4;  // one 4-byte copy per lane per wave
-constexpr int F8_STAGE = F8_ASTAGE + F8_BSTAGE + F8_SSTAGE;
-static_assert(F8_TBM == kTileM8, "row tile shared with the tile prefix scan");
-static_assert(F8_RPW % 4 == 0 && F8_RPW <= 64, "scale copy layout");
-static_assert(F8_NSTAGE * F8_STAGE <= 160 * 1024, "LDS per workgroup");
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-MOE_DEV int swz8(int row, int chunk) { return chunk ^ (row & 7); }
-
-// LDS float slot of row r's A scale within a stage's scale area
-MOE_DEV int scale_slot(int r) { return (r / F8_RPW) * 64 + (r % F8_RPW); }
-
-// 32 bytes (logical chunks c, c+1) of a staged row
-MOE_DEV i32x8 ld_frag8(const uint8_t* base, int row, int c) {
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + row * F8_TBK + (swz8(row, c) << 4));
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + row * F8_TBK + (swz8(row, c + 1) << 4));
-  return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
 
 // OCP E4M3FN code of a float32 value, round to nearest even, |v| clamped to 448
 MOE_DEV uint32_t e4m3_encode(float v) {
@@ -82,8 +34,6 @@ MOE_DEV uint32_t e4m3_encode(float v) {
   u += 0x7ffffu + ((u >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
   return sign | ((u >> 20) - (120u << 3));  // rebias the exponent 127 -> 7
 }
-
-MOE_DEV float max4(float a, float b, float c, float d) { return fmaxf(fmaxf(a, b), fmaxf(c, d)); }
 
 }  // namespace
 
@@ -135,19 +85,78 @@ hipError_t launch_quant_1x128(const bf16_t* x, long long rows, int C, uint8_t* q
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- fp8 tiled GEMM
+// ---------------------------------------------------------------- fp8 GEMM
+// Tile: kTileM8 (192) token rows x 256 weight rows.  Eight waves, two per
+// SIMD; wave w owns 32 weight rows (gate/up: 16 columns of W_gate and the
+// same 16 of W_up; down: 32 columns of W_down) against all 192 token rows, as
+// 12 x 2 blocks of v_mfma_scale_f32_16x16x128_f8f6f4.  One such MFMA covers a
+// whole 128-wide K block, so its result is the block's full-precision
+// partial product: it is scaled by (row scale * weight-block scale) and added
+// to the float32 accumulator at once (hardware block scales left at 1).
+//
+// Operand bytes: lane l holds, for its row (token or weight) l % 16, the two
+// 16-byte chunks g and g + 4 of the 128-byte block, g = l / 16.  Both
+// operands use the same lane -> K map, so the dot product is unchanged.
+//
+// Copies (buffer_load ... lds, 1 KB = 8 rows x 128 bytes per wave
+// instruction; chunk c of row r stored at position c ^ (r % 8)):
+//   - weight rows: each wave copies its own 32 rows into a private LDS ring
+//     of FS_NSB blocks; a block's stage is refilled as soon as the wave has
+//     read its fragments into registers, so FS_NSB blocks (96 KB per CU)
+//     are in flight while one is multiplied.  HBM's loaded latency of a few
+//     microseconds needs about that much to stream at full bandwidth;
+//   - token rows and their scales: shared by all waves, a ring of FS_NSA
+//     blocks, FS_NSA - 1 ahead (they mostly hit L2).
+// The waits are explicit vmcnt counts.  Per block kb: wait until this wave's
+// copies of kb have landed (a wave's copies complete in issue order; the
+// token rows of kb are issued one block before use, after the weight rows of
+// kb), workgroup barrier (everyone's token rows of kb are in LDS and everyone
+// is done with kb-1), read the weight fragments of kb, issue the token copies
+// of kb+1 into the stage of kb-1 and the weight copies of kb+FS_NSB into the
+// stage just read, multiply block kb.  Blocks past the end re-read the last
+// block so that every iteration issues the same copies.
+//
+// Gate/up tiles hold 128 columns of W_gate and the same 128 of W_up, exactly
+// one 1x128 slice of the SwiGLU output H: the epilogue forms SiLU(gate) * up,
+// reduces each row's max-abs across the eight waves through LDS, and writes H
+// as E4M3 codes plus one scale per row.
+//
+// What bounds it: the float32 promotion after every 128-wide K block costs
+// one multiply-add (and, gate/up, one multiply) per output element per block
+// on the vector ALUs, about as many lane-cycles as the MFMAs spend on the
+// block, and every wave reads all 192 token rows' fragments from LDS.  At
+// 4096 tokens the multiply side alone (no copies) measured 1.72 ms of the
+// gate/up GEMM's 2.4 ms, copies alone 1.86 ms; the weights stream at about
+// 3.2 TB/s.  Deeper copy rings (3 weight blocks in flight instead of 2) and
+// a per-workgroup rotation of the K order measured no faster.
+namespace {
+
+constexpr int FS_TBM = kTileM8;                  // token rows per tile
+constexpr int FS_RB = FS_TBM / 16;               // 16-row MFMA blocks
+constexpr int FS_TBN = 256;                      // weight rows per tile
+constexpr int FS_NWAVE = 8, FS_NTHREAD = 64 * FS_NWAVE;
+constexpr int FS_NSA = 2;                        // shared LDS stages of token rows
+constexpr int FS_NSB = 3;                        // private LDS stages of weight rows per wave
+constexpr int FS_ACOPY = FS_TBM / 8 / FS_NWAVE;  // 1 KB token-row copies per wave per block
+constexpr int FS_BCOPY = FS_TBN / 8 / FS_NWAVE;  // 1 KB weight-row copies per wave per block
+constexpr int FS_ASTAGE = FS_TBM * 128;          // code bytes per token stage
+constexpr int FS_STAGE = FS_ASTAGE + FS_TBM * 4; // + one float32 scale per row
+constexpr int FS_BWAVE = FS_BCOPY * 1024;        // bytes of one wave's weight block
+constexpr int FS_BBASE = FS_NSA * FS_STAGE;      // start of the weight rings
+constexpr int FS_ACOPIES = FS_ACOPY + 1;         // token-row copies + scale copy
+static_assert(FS_TBM == 192, "scale copies: three waves of 64 rows");
+static_assert(FS_TBM % 32 == 0 && (FS_TBM / 8) % FS_NWAVE == 0 && FS_BCOPY == 4, "tile configuration");
+static_assert(FS_BBASE + FS_NWAVE * FS_NSB * FS_BWAVE <= 160 * 1024, "LDS per workgroup");
+static_assert(FS_NSA == 2 && FS_NSB == 3, "the prologue and wait count below assume this ring");
+
+}  // namespace
+
 template <bool GATED>
-__global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 g) {
-  constexpr int AGRP = F8_TBM / 8;               // 1 KB copies (8 rows) of A per stage
-  constexpr int ACPW = AGRP / F8_NWAVE;
-  constexpr int BCPW = F8_TBN / 8 / F8_NWAVE;
-  constexpr int NJ = F8_TBN / F8_WN / 32;        // 32-column MFMA blocks per wave
-  static_assert(AGRP % F8_NWAVE == 0 && BCPW >= 1 && NJ == 2, "tile configuration");
-  constexpr int CPS = ACPW + BCPW + 1;           // copies per wave per stage (+1: scales)
+__global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
 
   // column tiles (N % 128 == 0; a down tile may be half past N)
-  const int n_nt = GATED ? g.N / (F8_TBN / 2) : (g.N + F8_TBN - 1) / F8_TBN;
+  const int n_nt = GATED ? g.N / (FS_TBN / 2) : (g.N + FS_TBN - 1) / FS_TBN;
   const int n_tasks = g.mt_start[g.n_exp] * n_nt;
   const int task = blockIdx.x;
   if (task >= n_tasks) return;  // uniform per workgroup, before any barrier
@@ -165,51 +174,66 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
   const bool shared = e >= g.E;
   const int cnt = shared ? g.T : g.counts[e];
   const int row_base = shared ? g.TK + (e - g.E) * g.T : g.offsets[e];
-  const int m0 = mtile * F8_TBM;
-  const int rows = min(F8_TBM, cnt - m0);
+  const int m0 = mtile * FS_TBM;
+  const int rows = min(FS_TBM, cnt - m0);
   const int K = g.K;
-  const int KB = K / 128;                        // scale blocks along K = stages
+  const int KB = K / 128;                        // scale blocks along K
   const int NB = g.N / 128;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / F8_WN, wn = wave % F8_WN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
 
-  // ---- copy sources (byte offsets from uniform bases; A offsets < T * K)
-  const uint8_t* __restrict__ abase = GATED ? g.a : g.a + (size_t)row_base * K;
-  const float* __restrict__ sabase = GATED ? g.as : g.as + (size_t)row_base * KB;
-  const uint8_t* __restrict__ wb0 = g.w0 + (size_t)e * g.N * K;
-  const uint8_t* __restrict__ wb1 = GATED ? g.w1 + (size_t)e * g.N * K : wb0;
+  // ---- token rows: buffer resources over the activation codes [T][K]
+  // (gate/up) or the staged rows from the expert's first one (down), and
+  // their scales [rows][K/128]
+  const int a_rows = GATED ? g.T : g.TK + (g.n_exp - g.E) * g.T - row_base;
+  const __amdgpu_buffer_rsrc_t ars =
+      buffer_rsrc(GATED ? g.a : g.a + (size_t)row_base * K, uint32_t(a_rows) * uint32_t(K));
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(GATED ? g.as : g.as + (size_t)row_base * KB,
+                                                 uint32_t(a_rows) * uint32_t(KB) * 4u);
   auto a_row = [&](int r) {  // activation row of tile row r (rows past the count re-read one)
     const int m = m0 + min(r, rows - 1);
     return GATED ? (shared ? m : g.perm[row_base + m]) : m;
   };
-  uint32_t aoff[ACPW], boff[BCPW];
+  // copy i of wave w fills tile rows 8 (FS_ACOPY w + i) .. +7; lane l writes
+  // LDS bytes 16 l of that 1 KB: row r0 + l/8 at position l%8, which holds
+  // logical chunk (l%8) ^ (row%8)
+  uint32_t aoff[FS_ACOPY];
 #pragma unroll
-  for (int i = 0; i < ACPW; ++i) {
-    const int r = 8 * (wave + F8_NWAVE * i) + (lane >> 3);
-    aoff[i] = uint32_t(a_row(r)) * uint32_t(K) + uint32_t(swz8(r, lane & 7) * 16);
+  for (int i = 0; i < FS_ACOPY; ++i) {
+    const int r = 8 * (FS_ACOPY * wave + i) + (lane >> 3);
+    aoff[i] = uint32_t(a_row(r)) * uint32_t(K) + uint32_t(((lane & 7) ^ (r & 7)) * 16);
   }
-#pragma unroll
-  for (int i = 0; i < BCPW; ++i) {
-    const int r = 8 * (wave * BCPW + i) + (lane >> 3);
-    // weight rows past N (a partial down tile) re-read row N-1; never stored
-    const int col =
-        GATED ? nt * (F8_TBN / 2) + (r & (F8_TBN / 2 - 1)) : min(nt * F8_TBN + r, g.N - 1);
-    boff[i] = uint32_t(col) * uint32_t(K) + uint32_t(swz8(r, lane & 7) * 16);
-  }
-  const uint8_t* __restrict__ wsrc = (GATED && wave >= F8_NWAVE / 2) ? wb1 : wb0;
-  // lane l copies the scale of row wave*RPW + l % RPW (lanes past RPW repeat)
-  const uint32_t soff = uint32_t(a_row(wave * F8_RPW + lane % F8_RPW)) * uint32_t(KB) * 4u;
+  // row scales: waves 0, 1, 2 copy rows 64 w + l; the other waves repeat
+  // wave 2's copy (the same bytes to the same LDS slots)
+  const int srow0 = 64 * min(wave, 2);
+  const uint32_t soff = uint32_t(a_row(srow0 + lane)) * uint32_t(KB) * 4u;
 
-  // weight-block scales of this wave's columns: gate/up tiles use block nt of
-  // s_gate and s_up; down tiles block (nt*256 + wn*64) / 128 of s_down
-  const float* __restrict__ sw0 = g.ws0 + (size_t)e * NB * KB +
-                                  (size_t)(GATED ? nt : min((nt * F8_TBN + wn * 64) / 128, NB - 1)) * KB;
+  // ---- weight rows of this wave (32: local row q = 16 j + c16 is MFMA
+  // column block j's row c16).  Gate/up: 16 columns of W_gate (rows 0-15)
+  // and the same 16 of W_up (rows 16-31); down: 32 columns (rows past N
+  // re-read row N-1 and are never stored).  Copy i covers local rows
+  // 8 i .. 8 i + 7.
+  const uint32_t wbytes = uint32_t(g.N) * uint32_t(K);
+  const __amdgpu_buffer_rsrc_t wr0 = buffer_rsrc(g.w0 + (size_t)e * g.N * K, wbytes);
+  const __amdgpu_buffer_rsrc_t wr1 = GATED ? buffer_rsrc(g.w1 + (size_t)e * g.N * K, wbytes) : wr0;
+  uint32_t boff[FS_BCOPY];
+#pragma unroll
+  for (int i = 0; i < FS_BCOPY; ++i) {
+    const int q = 8 * i + (lane >> 3);
+    const int wrow = GATED ? nt * 128 + 16 * wave + (q & 15)
+                           : min(nt * FS_TBN + 32 * wave + q, g.N - 1);
+    boff[i] = uint32_t(wrow) * uint32_t(K) + uint32_t(((lane & 7) ^ (q & 7)) * 16);
+  }
+
+  // weight-block scales of this wave's columns: gate/up use block nt of
+  // s_gate and s_up; down block (nt*256 + 32 w) / 128 of s_down.  Held in
+  // registers (lane l: blocks l and 64 + l) and read with v_readlane.
+  const float* __restrict__ sw0 =
+      g.ws0 + (size_t)e * NB * KB +
+      (size_t)(GATED ? nt : min((nt * FS_TBN + 32 * wave) / 128, NB - 1)) * KB;
   const float* __restrict__ sw1 = GATED ? g.ws1 + (size_t)e * NB * KB + (size_t)nt * KB : sw0;
-
-  // Held in registers before the pipeline starts (lane l: blocks l and 64 + l)
-  // and read with v_readlane: no vector load may be outstanding inside the
-  // pipeline, whose waits count only the LDS copies.
   float swv0[2], swv1[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -217,156 +241,168 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
     swv0[c] = sw0[kb];
     swv1[c] = sw1[kb];
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the counts below start from zero
 
-  const int mrows = rows - wm * 32 * F8_MBW;
-  const int mact =
-      __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : min(F8_MBW, (mrows + 31) >> 5));
+  // loop indices past the end repeat the last block
+  auto kblock = [&](int i) { return min(i, KB - 1); };
 
-  f32x16 acc[F8_MBW][NJ];
+  uint8_t* bring = smem8 + FS_BBASE + wave * FS_NSB * FS_BWAVE;  // this wave's weight ring
+  // token-row copies of block kb into shared stage kb % FS_NSA
+  auto copy_a = [&](int kb) {
+    const uint32_t kc = uint32_t(kblock(kb));
+    uint8_t* st = smem8 + (kb % FS_NSA) * FS_STAGE;
 #pragma unroll
-  for (int i = 0; i < F8_MBW; ++i)
+    for (int i = 0; i < FS_ACOPY; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ars, (lds_void*)(st + 8 * (FS_ACOPY * wave + i) * 128), 16, aoff[i] + kc * 128u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)(st + FS_ASTAGE + srow0 * 4), 4,
+                                             soff + kc * 4u, 0, 0, 0);
+  };
+  // weight-row copies of block kb into private stage kb % FS_NSB
+  auto copy_b = [&](int kb) {
+    const uint32_t ko = uint32_t(kblock(kb)) * 128u;
+    uint8_t* st = bring + (kb % FS_NSB) * FS_BWAVE;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  int brow0[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    brow0[j] = GATED ? ((j < NJ / 2) ? (wn * (F8_TBN / 2 / F8_WN) + 32 * j)
-                                     : (F8_TBN / 2 + wn * (F8_TBN / 2 / F8_WN) + 32 * (j - NJ / 2)))
-                     : (wn * (F8_TBN / F8_WN) + 32 * j);
-  const int arow0 = wm * 32 * F8_MBW + (lane & 31);
-
-  auto copy_step = [&](int kt) {
-    const int kc = min(kt, KB - 1);
-    const uint32_t koff = uint32_t(kc * F8_TBK);
-    uint8_t* st = smem8 + (kt % F8_NSTAGE) * F8_STAGE;
-    uint8_t* a = st + (8 * wave) * F8_TBK;
-    uint8_t* b = st + F8_ASTAGE + (8 * BCPW * wave) * F8_TBK;
-    uint8_t* s = st + F8_ASTAGE + F8_BSTAGE + wave * 256;
-#pragma unroll
-    for (int i = 0; i < ACPW; ++i)
-      __builtin_amdgcn_global_load_lds(abase + (aoff[i] + koff),
-                                       (lds_void*)(a + 8 * F8_NWAVE * i * F8_TBK), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BCPW; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc + (boff[i] + koff), (lds_void*)(b + 8 * i * F8_TBK), 16,
-                                       0, 0);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(sabase) + (soff + kc * 4u),
-                                     (lds_void*)s, 4, 0, 0);
+    for (int i = 0; i < FS_BCOPY; ++i) {
+      const __amdgpu_buffer_rsrc_t rs = (GATED && i >= FS_BCOPY / 2) ? wr1 : wr0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + 1024 * i), 16, boff[i] + ko, 0,
+                                               0, 0);
+    }
   };
 
-  const f32x16 zero = {};
-  auto compute = [&](int kt, auto mact_c) {
-    constexpr int MACT = decltype(mact_c)::value;
-    const uint8_t* st = smem8 + (kt % F8_NSTAGE) * F8_STAGE;
-    const uint8_t* a = st;
-    const uint8_t* b = st + F8_ASTAGE;
-    const float* sc = reinterpret_cast<const float*>(st + F8_ASTAGE + F8_BSTAGE);
+  const int mact = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);  // active 32-row pairs
+  f32x4 acc[FS_RB][2];
+#pragma unroll
+  for (int i = 0; i < FS_RB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // 32 bytes of operand row r of a staged block: chunks g4 and g4 + 4
+  auto frag = [&](const uint8_t* base, int r) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + r * 128 + ((g4 ^ (r & 7)) << 4));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + r * 128 + (((g4 + 4) ^ (r & 7)) << 4));
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+  auto compute = [&](int kb, const i32x8& b0, const i32x8& b1, auto mact_c) {
+    constexpr int NRB = 2 * decltype(mact_c)::value;
+    const uint8_t* st = smem8 + (kb % FS_NSA) * FS_STAGE;
+    const float* sc = reinterpret_cast<const float*>(st + FS_ASTAGE);
+    const int kr = kblock(kb);
     const float sb0 = __int_as_float(
-        __builtin_amdgcn_readlane(__float_as_int(kt < 64 ? swv0[0] : swv0[1]), kt & 63));
+        __builtin_amdgcn_readlane(__float_as_int(kr < 64 ? swv0[0] : swv0[1]), kr & 63));
     const float sb1 = __int_as_float(
-        __builtin_amdgcn_readlane(__float_as_int(kt < 64 ? swv1[0] : swv1[1]), kt & 63));
-    i32x8 bf[2][NJ];
+        __builtin_amdgcn_readlane(__float_as_int(kr < 64 ? swv1[0] : swv1[1]), kr & 63));
+    // token fragments and row scales are read two row blocks ahead of their
+    // MFMAs; scheduling barriers keep the reads there
+    i32x8 af[NRB];
+    f32x4 sa[NRB];
+    auto rd = [&](int i) {
+      af[i] = frag(st, 16 * i + c16);
+      sa[i] = *reinterpret_cast<const f32x4*>(sc + 16 * i + 4 * g4);
+    };
+    rd(0);
+    if (NRB > 1) rd(1);
+    const float sbb = GATED ? sb1 : sb0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < NRB; ++i) {
+      if (i + 2 < NRB) rd(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 t0 =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], b0, zero, 0, 0, 0, 127, 0, 127);
+      const f32x4 t1 =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], b1, zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bf[h][j] = ld_frag8(b, brow0[j] + (lane & 31), 4 * h + 2 * (lane >> 5));
-#pragma unroll
-    for (int i = 0; i < MACT; ++i) {
-      const i32x8 a0 = ld_frag8(a, arow0 + 32 * i, 2 * (lane >> 5));
-      const i32x8 a1 = ld_frag8(a, arow0 + 32 * i, 4 + 2 * (lane >> 5));
-      f32x4 sa[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sa[q] = *reinterpret_cast<const f32x4*>(
-            sc + scale_slot(wm * 32 * F8_MBW + 32 * i + 8 * q + 4 * (lane >> 5)));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        f32x16 t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bf[0][j], zero, 0, 0, 0,
-                                                                   127, 0, 127);
-        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bf[1][j], t, 0, 0, 0, 127, 0, 127);
-        const float sbj = (GATED && j >= NJ / 2) ? sb1 : sb0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(t[v], sa[v >> 2][v & 3] * sbj, acc[i][j][v]);
+      for (int v = 0; v < 4; ++v) {
+        acc[i][0][v] = fmaf(t0[v], sa[i][v] * sb0, acc[i][0][v]);
+        acc[i][1][v] = fmaf(t1[v], sa[i][v] * sbb, acc[i][1][v]);
       }
     }
   };
 
-  // pipeline as in the bf16 tiled GEMM: copies run NSTAGE-1 blocks ahead;
-  // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt/lgkmcnt at maxima
-  constexpr int VMWAIT = (F8_NSTAGE - 2) * CPS;
-  static_assert(VMWAIT < 64, "vmcnt field is 6 bits");
-  constexpr int WAITIMM = (VMWAIT & 15) | ((VMWAIT >> 4) << 14) | 0x70 | 0xf00;
+  // Issue order (W = weight rows, A = token rows and scales):
+  //   prologue W0 W1 A0 W2; block kb: A(kb+1) W(kb+3)
+  // At the top of block kb the copies issued after A(kb) are exactly one
+  // weight block (W(kb+2)), and W(kb) was issued before A(kb): waiting until
+  // at most FS_BCOPY copies are in flight completes both.  The wave then
+  // reads its weight fragments of kb into registers, which frees its weight
+  // stage of kb for W(kb+3): three weight blocks stay in flight.
+  // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt/lgkmcnt at maxima.
+  constexpr int VMW = FS_BCOPY;
+  constexpr int WAITIMM = (VMW & 15) | ((VMW >> 4) << 14) | 0x70 | 0xf00;
   auto mainloop = [&](auto mact_c) {
-#pragma unroll
-    for (int p = 0; p < F8_NSTAGE - 1; ++p) copy_step(p);
-    for (int kt = 0; kt < KB; ++kt) {
-      __builtin_amdgcn_s_waitcnt(WAITIMM);
-      __builtin_amdgcn_s_barrier();
-      copy_step(kt + F8_NSTAGE - 1);
-      compute(kt, mact_c);
+    copy_b(0);
+    copy_b(1);
+    copy_a(0);
+    copy_b(2);
+    for (int kb = 0; kb < KB; ++kb) {
+      __builtin_amdgcn_s_waitcnt(WAITIMM);  // this wave's token and weight rows of kb landed
+      __builtin_amdgcn_s_barrier();         // everyone's; everyone is done with kb-1
+      const uint8_t* bst = bring + (kb % FS_NSB) * FS_BWAVE;
+      const i32x8 b0 = frag(bst, c16), b1 = frag(bst, 16 + c16);
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the weight stage of kb is free
+      copy_a(kb + 1);                       // into the token stage of kb-1
+      copy_b(kb + FS_NSB);                  // into this wave's weight stage of kb
+      compute(kb, b0, b1, mact_c);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   };
-  static_assert(F8_MBW <= 4, "dispatch below covers up to 4 blocks");
   switch (mact) {
-    case 4: mainloop(std::integral_constant<int, (F8_MBW >= 4 ? 4 : 0)>{}); break;
-    case 3: mainloop(std::integral_constant<int, (F8_MBW >= 3 ? 3 : 0)>{}); break;
+    case 6: mainloop(std::integral_constant<int, 6>{}); break;
+    case 5: mainloop(std::integral_constant<int, 5>{}); break;
+    case 4: mainloop(std::integral_constant<int, 4>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
     case 2: mainloop(std::integral_constant<int, 2>{}); break;
-    case 1: mainloop(std::integral_constant<int, 1>{}); break;
-    default: mainloop(std::integral_constant<int, 0>{}); break;
+    default: mainloop(std::integral_constant<int, 1>{}); break;
   }
 
-  // ---- epilogue.  32x32 accumulator v of lane l: row 8*(v/4) + 4*(l/32) + v%4,
-  // column l%32
+  // ---- epilogue.  16x16 accumulator v of lane l: row 4*(l/16) + v, column l%16
   if (GATED) {
     // H = SiLU(gate) * up for the tile's 128 columns (one 1x128 slice per row)
-    float* red = reinterpret_cast<float*>(smem8);  // [WN][TBM] row max-abs per column wave
+    float* red = reinterpret_cast<float*>(smem8);  // [NWAVE][TBM] row max-abs per wave
     __syncthreads();  // every wave is done with the staged operands
-    float h[F8_MBW][16];
+    f32x4 h[FS_RB];
 #pragma unroll
-    for (int i = 0; i < F8_MBW; ++i) {
-      if (i >= mact) break;
+    for (int i = 0; i < FS_RB; ++i) {
+      if (2 * mact <= i) continue;  // uniform
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 4; ++v) {
         h[i][v] = siluf(acc[i][0][v]) * acc[i][1][v];
         float m = fabsf(h[i][v]);
 #pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        const int r = wm * 32 * F8_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if ((lane & 31) == 0) red[wn * F8_TBM + r] = m;
+        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+        if (c16 == 0) red[wave * FS_TBM + 16 * i + 4 * g4 + v] = m;
       }
     }
     __syncthreads();
-    const int col = nt * 128 + wn * 32 + (lane & 31);
+    const int col = nt * 128 + 16 * wave + c16;
 #pragma unroll
-    for (int i = 0; i < F8_MBW; ++i) {
-      if (i >= mact) break;
+    for (int i = 0; i < FS_RB; ++i) {
+      if (2 * mact <= i) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 32 * F8_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const float amax = max4(red[r], red[F8_TBM + r], red[2 * F8_TBM + r], red[3 * F8_TBM + r]);
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * i + 4 * g4 + v;
+        float amax = 0.f;
+#pragma unroll
+        for (int w = 0; w < FS_NWAVE; ++w) amax = fmaxf(amax, red[w * FS_TBM + r]);
         const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
         if (r < rows) {
           const size_t orow = (size_t)(row_base + m0 + r);
           g.out8[orow * g.N + col] = uint8_t(e4m3_encode(h[i][v] / scale));
-          if (wn == 0 && (lane & 31) == 0) g.out_s[orow * NB + nt] = scale;
+          if (wave == 0 && c16 == 0) g.out_s[orow * NB + nt] = scale;
         }
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < F8_MBW; ++i) {
-      if (i >= mact) break;
+    for (int i = 0; i < FS_RB; ++i) {
+      if (2 * mact <= i) continue;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int col = nt * F8_TBN + wn * (F8_TBN / F8_WN) + 32 * j + (lane & 31);
+      for (int j = 0; j < 2; ++j) {
+        const int col = nt * FS_TBN + 32 * wave + 16 * j + c16;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * 32 * F8_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        for (int v = 0; v < 4; ++v) {
+          const int r = 16 * i + 4 * g4 + v;
           if (r < rows && col < g.N)
             g.out16[(size_t)(row_base + m0 + r) * g.N + col] = f32_to_bf16(acc[i][j][v]);
         }
@@ -375,11 +411,11 @@ __global__ __launch_bounds__(F8_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
   }
 }
 
-size_t tile_gemm_fp8_lds_bytes() { return size_t(F8_NSTAGE) * F8_STAGE; }
+size_t tile_gemm_fp8_lds_bytes() { return size_t(FS_BBASE) + size_t(FS_NWAVE) * FS_NSB * FS_BWAVE; }
 
 template <bool GATED>
 static hipError_t launch_fp8_one(const TileArgs8& g, int max_mtiles, hipStream_t st) {
-  const int n_nt = GATED ? g.N / (F8_TBN / 2) : (g.N + F8_TBN - 1) / F8_TBN;
+  const int n_nt = GATED ? g.N / (FS_TBN / 2) : (g.N + FS_TBN - 1) / FS_TBN;
   const long long blocks = (long long)max_mtiles * n_nt;
   if (blocks <= 0) return hipSuccess;
   const size_t lds = tile_gemm_fp8_lds_bytes();
@@ -391,7 +427,7 @@ static hipError_t launch_fp8_one(const TileArgs8& g, int max_mtiles, hipStream_t
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm_fp8_kernel<GATED>), dim3((unsigned)blocks), dim3(F8_NTHREAD), lds,
+  hipLaunchKernelGGL((tile_gemm_fp8_kernel<GATED>), dim3((unsigned)blocks), dim3(FS_NTHREAD), lds,
                      st, g);
   return hipGetLastError();
 }

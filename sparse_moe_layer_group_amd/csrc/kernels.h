@@ -103,10 +103,7 @@ struct TileArgs8 {
   const int32_t* mt_start;    // [E+S+1] prefix of kTileM8-row tiles
   int E, n_exp, T, TK, N, K;
 };
-#ifndef MOE_F8_MBW
-#define MOE_F8_MBW 3  // 32-row MFMA blocks per wave of the fp8 tiled GEMM (2 waves along M)
-#endif
-constexpr int kTileM8 = 64 * MOE_F8_MBW;
+constexpr int kTileM8 = 192;  // token rows per tile of the fp8 GEMM
 hipError_t launch_tile_gemm_fp8(const TileArgs8& g, bool gated, int max_mtiles, hipStream_t st);
 
 // ---- sequence-wise balance loss (balance_kernels.hip)
