@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // Router logits for large batches: an LDS-tiled bf16 GEMM over K = 3H.
 // Workgroup tile 128 tokens x 256 experts, split along K into `chunks` parts
 // (P[c][t][e], added in order by the select kernel).  K steps of 32 staged by
-// direct global->LDS copies three steps ahead into four stages (24 KB each);
+// direct global->LDS copies (buffer_load ... lds) three steps ahead into four
+// stages (24 KB each);
 // the activation row of step kt is x[t][kt*32 mod H ..].  Eight waves in
 // 2 x 4, each 64 x 64 as 2 x 2 MFMA 32x32x16 blocks.  Staged rows are 64 bytes
 // (four 16-byte chunks at chunk ^ ((row/2) % 4)).
@@ -174,7 +175,6 @@ namespace {
 constexpr int RT_TBM = 128, RT_TBN = 256, RT_TBK = 32, RT_NSTAGE = 4;
 constexpr int RT_NWAVE = 8, RT_WN = 4;
 constexpr int RT_ASTAGE = RT_TBM * RT_TBK, RT_BSTAGE = RT_TBN * RT_TBK;  // bf16 elements
-typedef __attribute__((address_space(3))) void rt_lds_void;
 MOE_DEV int rt_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 }  // namespace
 
@@ -193,7 +193,8 @@ __global__ __launch_bounds__(512, 1) void router_tile_kernel(const bf16_t* __res
   const int kt0 = c * steps_per_chunk;
   const int nk = min(steps_per_chunk, nsteps_all - kt0);
   const int rows = min(RT_TBM, T - t0), cols = min(RT_TBN, E - e0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / RT_WN, wn = wave % RT_WN;
   const int spp = H / RT_TBK;  // steps per part
 
@@ -204,14 +205,16 @@ __global__ __launch_bounds__(512, 1) void router_tile_kernel(const bf16_t* __res
     const int t = t0 + min(r, rows - 1);
     aoff[i] = (uint32_t(t) * uint32_t(H) + uint32_t(rt_swz(r, lane & 3) * 8)) * 2u;
   }
-  const char* __restrict__ bbase = reinterpret_cast<const char*>(wt3 + (size_t)e0 * 3 * H);
+  // buffer resources over x [T][H] and the split router rows e0.. of Wt3 [E][3H]
+  const __amdgpu_buffer_rsrc_t brs =
+      buffer_rsrc(wt3 + (size_t)e0 * 3 * H, uint32_t(E - e0) * uint32_t(3 * H) * 2u);
+  const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(x, uint32_t(T) * uint32_t(H) * 2u);
 #pragma unroll
   for (int i = 0; i < BCPW; ++i) {
     const int r = 16 * (wave * BCPW + i) + (lane >> 2);
     const int e = min(r, cols - 1);
     boff[i] = (uint32_t(e) * uint32_t(3 * H) + uint32_t(rt_swz(r, lane & 3) * 8)) * 2u;
   }
-  const char* __restrict__ abase = reinterpret_cast<const char*>(x);
 
   auto copy_step = [&](int j) {
     const int kt = kt0 + min(j, nk - 1);
@@ -222,13 +225,9 @@ __global__ __launch_bounds__(512, 1) void router_tile_kernel(const bf16_t* __res
     bf16_t* a = As + stage * RT_ASTAGE + (16 * ACPW * wave) * RT_TBK;
     bf16_t* b = Bs + stage * RT_BSTAGE + (16 * BCPW * wave) * RT_TBK;
 #pragma unroll
-    for (int i = 0; i < ACPW; ++i)
-      __builtin_amdgcn_global_load_lds(abase + (aoff[i] + ka), (rt_lds_void*)(a + 16 * i * RT_TBK),
-                                       16, 0, 0);
+    for (int i = 0; i < ACPW; ++i) copy16_to_lds(ars, aoff[i] + ka, a + 16 * i * RT_TBK);
 #pragma unroll
-    for (int i = 0; i < BCPW; ++i)
-      __builtin_amdgcn_global_load_lds(bbase + (boff[i] + kb), (rt_lds_void*)(b + 16 * i * RT_TBK),
-                                       16, 0, 0);
+    for (int i = 0; i < BCPW; ++i) copy16_to_lds(brs, boff[i] + kb, b + 16 * i * RT_TBK);
   };
 
   f32x16 acc[2][2];
