@@ -40,22 +40,26 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> gemm_gate_up counters per launch
-    "decode": {"src_sha256": "4709ad78f470104197d7a133802d3726b11ed05c8f6c3d1fcd2b0be09fcc984c",
-               "fetch_kib": 8153487.2, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "4709ad78f470104197d7a133802d3726b11ed05c8f6c3d1fcd2b0be09fcc984c",
-                "fetch_kib": 12336734.0, "write_kib": 294912.6},
+    "decode": {"src_sha256": "c875e62590295a1f87d56ac298a1e004947bd7d8f21c5abc0788659ce6399ed5",
+               "fetch_kib": 8153779.9, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "b2a33c33e215b2456d61a803fa6107fe51b8ff34dad7e115e445688407780812",
+                "fetch_kib": 12314692.0, "write_kib": 294912.2},
 }
-KERNEL_SOURCES = ("common.h", "kernels.h", "moe_api.cpp", "route_kernels.hip",
-                  "gemm_kernels.hip", "stream_gemm.hip", "tile_gemm.hip", "fp8_kernels.hip")
+# sources the gate/up kernel of each workload is built and launched from
+_COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
+KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
+                  "prefill": _COMMON_SOURCES + ("tile_gemm.hip",),
+                  "skew": _COMMON_SOURCES + ("stream_gemm.hip", "tile_gemm.hip"),
+                  "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",)}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(workload):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[workload]:
         with open(os.path.join(ROOT, "sparse_moe_layer_group_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -64,7 +68,7 @@ def kernel_sources_sha256():
 def measured_traffic(workload):
     """HBM bytes per launch of gemm_gate_up, or None when not measured for the current sources."""
     t = MEASURED_TRAFFIC.get(workload)
-    if not t or not COPY_CALIBRATION or t["src_sha256"] != kernel_sources_sha256():
+    if not t or not COPY_CALIBRATION or t["src_sha256"] != kernel_sources_sha256(workload):
         return None
     return int(t["fetch_kib"] * COPY_CALIBRATION["fetch_bytes_per_kib"] +
                t["write_kib"] * COPY_CALIBRATION["write_bytes_per_kib"])
