@@ -13,9 +13,10 @@ and section:
   [V3]   "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token"
          (PaperTrace close reading of the DeepSeek-V3 technical report)
          §1.1 shapes; §1.3 sigmoid gating and node-limited routing (Eq 12,
-         13, 15); §1.4 auxiliary-loss-free balancing (Eq 16) and the
-         sequence-wise balance loss (Eq 17-20); §2.2 FP8
-         fine-grained quantisation; §5.1 deployment (shared expert as an
+         13, 15); §1.4 auxiliary-loss-free balancing (Eq 16; the bias takes
+         no part in backpropagation) and the sequence-wise balance loss
+         (Eq 17-20); §2.2 FP8 fine-grained quantisation and the recomputed
+         SwiGLU output in the backward; §5.1 deployment (shared expert as an
          always-selected expert).
   [DEP]  "DeepSeek-V3 复盘：MoE、MLA、FP8 与低成本叙事如何验算" (audit of the
          report's cost and deployment claims; the released weights are FP8).
@@ -39,6 +40,10 @@ Parity status of each function (what pins it in tests/test_oracle_*.py):
   sequence_balance_loss pinned (closed forms for balanced and uniform
                         affinities; sum f = E, sum P = 1; scalar-loop brute force)
   e4m3_* / quantize_1x128  pinned (all 256 codes; torch float8_e4m3fn)
+  backward and its parts  pinned (central finite differences of
+                        layer_fixed_routing in every input; torch CPU autograd
+                        of the fixed-routing layer; zero router gradient with
+                        one routed expert; linearity in dy)
 """
 from __future__ import annotations
 
@@ -319,6 +324,200 @@ def forward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: ExpertS
     if residual is not None:
         y += lift(residual)[tok]
     return ForwardResult(y=y, tokens=tok, routing=r, perm=p)
+
+
+# ----------------------------------------------------------------------------
+# backward of the layer for one training step ([V3] §1.3 Eq 12-15, §1.4, §2.2)
+# ----------------------------------------------------------------------------
+#
+# The gradients are those of the scalar <dy, y> for an upstream gradient dy of
+# the layer output y (the MoE branch).  Readings:
+#   - the selection of experts is a discrete choice and carries no gradient;
+#     the bias enters only the selection and takes no part in
+#     backpropagation ([V3] §1.4 says so explicitly), so it has no gradient;
+#   - the gates are the normalised raw affinities of the chosen experts
+#     ([V3] §1.3 Eq 13), and their gradient flows through the normalisation
+#     and the sigmoid into the router logits, hence into x and W_r;
+#   - the function differentiated is the layer in float64 with the selection
+#     held fixed (``layer_fixed_routing``); the selection itself is the
+#     forward's (float32 scores with the bias).
+
+def dsilu(v: np.ndarray) -> np.ndarray:
+    """Derivative of SiLU(v) = v * sigmoid(v): sigmoid(v) * (1 + v * (1 - sigmoid(v)))."""
+    sg = 1.0 / (1.0 + np.exp(-v))
+    return sg * (1.0 + v * (1.0 - sg))
+
+
+def layer_fixed_routing(x64: np.ndarray, wr64: np.ndarray, idx: np.ndarray, experts: ExpertSource,
+                        n_shared: int = 1) -> np.ndarray:
+    """The layer output in float64 as a smooth function of x, W_r and the
+    expert weights, for a fixed choice of experts ``idx`` [T][K].
+
+    [V3] §1.3 Eq 12, 13, 15: y_t = sum over shared experts of FFN(x_t) +
+    sum_k g_tk FFN_{e_k}(x_t), g_tk = s_{t,e_k} / sum_j s_{t,e_j},
+    s = sigmoid(x W_r) (no float32 rounding here).
+    """
+    T = x64.shape[0]
+    E = wr64.shape[1]
+    s = 1.0 / (1.0 + np.exp(-(x64 @ wr64)))
+    ssel = np.take_along_axis(s, idx, axis=1)
+    g = ssel / ssel.sum(axis=1, keepdims=True)
+    y = np.zeros_like(x64)
+    for e in sorted(set(int(v) for v in idx.reshape(-1))):
+        jj, kk = np.nonzero(idx == e)
+        wg, wu, wd = expert_f64(experts(e))
+        y[jj] += g[jj, kk][:, None] * expert_ffn(x64[jj], wg, wu, wd)
+    for sh in range(n_shared):
+        wg, wu, wd = expert_f64(experts(E + sh))
+        y += expert_ffn(x64, wg, wu, wd)
+    return y
+
+
+def expert_backward(X: np.ndarray, dY: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray):
+    """Backward of one SwiGLU expert Y = (SiLU(X W_gate^T) * (X W_up^T)) W_down^T.
+
+    [V3] §1.1 (the three matrices) and §2.2 (the SwiGLU input is kept and its
+    output recomputed in the backward): with G = X W_gate^T, U = X W_up^T,
+    A = SiLU(G), H = A * U,
+      dH = dY W_down,      dW_down = dY^T H,
+      dU = dH * A,         dG = dH * U * SiLU'(G),
+      dX = dG W_gate + dU W_up,  dW_gate = dG^T X,  dW_up = dU^T X.
+    Returns (dX, dW_gate, dW_up, dW_down), float64.
+    """
+    G = X @ wg.T
+    U = X @ wu.T
+    A = silu(G)
+    Hh = A * U
+    dH = dY @ wd
+    dwd = dY.T @ Hh
+    dU = dH * A
+    dG = dH * U * dsilu(G)
+    dX = dG @ wg + dU @ wu
+    return dX, dG.T @ X, dU.T @ X, dwd
+
+
+def gate_backward(ssel: np.ndarray, dg: np.ndarray) -> np.ndarray:
+    """Gradient of the router logits of the chosen experts from the gate gradients.
+
+    [V3] §1.3 Eq 13 and 15: g_k = s_k / S with S = sum_j s_j over the chosen
+    experts and s = sigmoid(L).  Then ds_j = (dg_j - sum_k dg_k g_k) / S and
+    dL_j = ds_j s_j (1 - s_j); the logits of experts not chosen get no gradient.
+    ``ssel`` and ``dg`` are [T][K]; returns dL [T][K].
+    """
+    S = ssel.sum(axis=1, keepdims=True)
+    g = ssel / S
+    ds = (dg - (dg * g).sum(axis=1, keepdims=True)) / S
+    return ds * ssel * (1.0 - ssel)
+
+
+@dataclass
+class BackwardResult:
+    dx: np.ndarray                 # [len(tokens)][H] float64
+    tokens: np.ndarray             # token ids the rows of dx belong to
+    dw_router: np.ndarray          # [H][E] float64 (columns of router_cols, others 0)
+    dw: Dict[int, tuple]           # expert id -> (dW_gate, dW_up, dW_down), float64
+    dgate: np.ndarray              # [T][K] float64 gate gradients (rows of grad_tokens)
+    dlogit: np.ndarray             # [T][K] float64 logit gradients of the chosen experts
+    routing: Routing
+    perm: Perm
+
+
+def backward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: ExpertSource,
+             dy64: np.ndarray, *, n_groups: int, topk_groups: int, topk: int, group_topn: int = 2,
+             n_shared: int = 1, tokens: Optional[Sequence[int]] = None,
+             grad_experts: Optional[Sequence[int]] = None,
+             router_cols: Optional[Sequence[int]] = None) -> BackwardResult:
+    """Gradients of <dy, y> w.r.t. x, W_r and every expert's three matrices.
+
+    Steps, in the order of the forward they reverse ([V3] §1.3 Eq 12-15):
+      1. route as the forward does (selection with the bias, [V3] §1.4);
+      2. per chosen expert, its output Y_k(x_t) and the gate gradient
+         dg_tk = <dy_t, Y_k(x_t)> (Eq 12);
+      3. logit gradients of the chosen experts through the gate
+         normalisation and the sigmoid (``gate_backward``);
+      4. router: dx_t += sum_k dL_tk W_r[:, e_k]; dW_r[:, e] = sum over the
+         assignments (t, k) to e of dL_tk x_t;
+      5. each expert's backward with dY = g_tk dy_t on its rows (the shared
+         expert: dY = dy_t on every row), dx_t += its dX rows (``expert_backward``).
+    Float64 throughout on float64 affinities s = sigmoid(x W_r).
+
+    Subsets for large shapes: ``tokens`` (rows of dx), ``grad_experts``
+    (experts whose weight gradients are formed; shared = E), ``router_cols``
+    (columns of dW_r).  Gate and logit gradients are formed for the tokens
+    these need.  Defaults: everything.
+    """
+    T, H = x64.shape
+    E = wr64.shape[1]
+    L, s32, r, p = route(x64, wr64, b32, n_groups=n_groups, topk_groups=topk_groups, topk=topk,
+                         group_topn=group_topn)
+    idx = r.idx.astype(np.int64)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    gexp = list(range(E + n_shared)) if grad_experts is None else [int(e) for e in grad_experts]
+    rcols = list(range(E)) if router_cols is None else [int(e) for e in router_cols]
+
+    # tokens whose logit gradients are needed: rows of dx, and every token
+    # routed to a column of dW_r
+    need = set(int(t) for t in tok)
+    for e in rcols:
+        need.update(int(t) for t in np.nonzero((idx == e).any(axis=1))[0])
+    need = np.array(sorted(need), dtype=np.int64)
+
+    s = 1.0 / (1.0 + np.exp(-(x64 @ wr64)))
+    ssel = np.take_along_axis(s, idx, axis=1)
+    g = ssel / ssel.sum(axis=1, keepdims=True)
+
+    # step 2: gate gradients of the needed tokens
+    dg = np.zeros((T, topk), dtype=F64)
+    if len(need):
+        sel = idx[need]
+        for e in sorted(set(int(v) for v in sel.reshape(-1))):
+            jj, kk = np.nonzero(sel == e)
+            wg, wu, wd = expert_f64(experts(e))
+            Y = expert_ffn(x64[need[jj]], wg, wu, wd)
+            dg[need[jj], kk] = np.einsum("rh,rh->r", dy64[need[jj]], Y)
+    # step 3
+    dL = np.zeros((T, topk), dtype=F64)
+    dL[need] = gate_backward(ssel[need], dg[need])
+
+    # step 4: router
+    dx = np.zeros((len(tok), H), dtype=F64)
+    for k in range(topk):
+        dx += dL[tok, k][:, None] * wr64[:, idx[tok, k]].T
+    dwr = np.zeros((H, E), dtype=F64)
+    for e in rcols:
+        tt, kk = np.nonzero(idx == e)
+        dwr[:, e] = (dL[tt, kk][:, None] * x64[tt]).sum(axis=0)
+
+    # step 5: experts.  Weight gradients need all rows of the expert; dx needs
+    # the rows of the requested tokens.
+    pos = {int(t): i for i, t in enumerate(tok)}
+    dw = {}
+    sel_tok = idx[tok]
+    for e in sorted(set(int(v) for v in sel_tok.reshape(-1)) | set(gexp)):
+        wg, wu, wd = expert_f64(experts(e))
+        if e >= E:                                  # shared: every token, dY = dy
+            rows = np.arange(T) if e in gexp else tok
+            dY = dy64[rows]
+        else:
+            tt, kk = np.nonzero(idx == e)
+            if e not in gexp:                       # only the requested tokens' rows
+                keep = np.isin(tt, tok)
+                tt, kk = tt[keep], kk[keep]
+            rows = tt
+            dY = g[tt, kk][:, None] * dy64[tt]
+        if len(rows) == 0:
+            if e in gexp:
+                dw[e] = (np.zeros_like(wg), np.zeros_like(wu), np.zeros_like(wd))
+            continue
+        dX, dwg, dwu, dwd = expert_backward(x64[rows], dY, wg, wu, wd)
+        if e in gexp:
+            dw[e] = (dwg, dwu, dwd)
+        for i, t in enumerate(rows):
+            j = pos.get(int(t))
+            if j is not None:
+                dx[j] += dX[i]
+    return BackwardResult(dx=dx, tokens=tok, dw_router=dwr, dw=dw, dgate=dg, dlogit=dL,
+                          routing=r, perm=p)
 
 
 # ----------------------------------------------------------------------------

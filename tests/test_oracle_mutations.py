@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 import oracle.moe_oracle as M
+from tests import test_oracle_backward as TBW
 from tests import test_oracle_balance as TB
 from tests import test_oracle_ffn as TF
 from tests import test_oracle_fp8 as T8
@@ -22,7 +23,8 @@ def _patch(monkeypatch, name, fn):
 _orig = {n: getattr(M, n) for n in ("group_scores", "biased_scores", "gate_values", "permute",
                                      "expert_ffn", "bias_update", "router_affinity",
                                      "e4m3_quantize", "select_experts",
-                                     "sequence_balance_loss")}
+                                     "sequence_balance_loss", "dsilu", "gate_backward",
+                                     "expert_backward")}
 
 
 def m_group_top1(z, n_groups, group_topn):
@@ -99,6 +101,20 @@ def m_bal_smallest(s, K, seq_len, alpha):
     return M.BalanceLoss(loss=alpha * (f * r.P).sum(axis=1), f=f, P=r.P, gap=r.gap)
 
 
+def m_dsilu_sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def m_gate_bwd_uncentred(ssel, dg):
+    S = ssel.sum(axis=1, keepdims=True)
+    return dg / S * ssel * (1.0 - ssel)
+
+
+def m_expert_bwd_swapped(X, dY, wg, wu, wd):
+    dX, dwg, dwu, dwd = _orig["expert_backward"](X, dY, wg, wu, wd)
+    return dX, dwu, dwg, dwd
+
+
 CASES = [
     ("group_scores", m_group_top1, TR.test_selection_matches_subset_enumeration, (0,)),
     ("biased_scores", m_no_bias, TR.test_large_bias_forces_and_excludes_experts, ()),
@@ -114,6 +130,10 @@ CASES = [
     ("sequence_balance_loss", m_bal_raw_P, TB.test_balanced_selection_gives_alpha, ()),
     ("sequence_balance_loss", m_bal_no_scale, TB.test_balanced_selection_gives_alpha, ()),
     ("sequence_balance_loss", m_bal_smallest, TB.test_concentrated_routing_is_penalised, ()),
+    ("dsilu", m_dsilu_sigmoid, TBW.test_directional_derivatives_match_finite_differences, ("x",)),
+    ("gate_backward", m_gate_bwd_uncentred, TBW.test_directional_derivatives_match_finite_differences,
+     ("w_router",)),
+    ("expert_backward", m_expert_bwd_swapped, TBW.test_gradients_match_torch_autograd, ()),
 ]
 
 
