@@ -493,7 +493,8 @@ def backward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: Expert
     pos = {int(t): i for i, t in enumerate(tok)}
     dw = {}
     sel_tok = idx[tok]
-    for e in sorted(set(int(v) for v in sel_tok.reshape(-1)) | set(gexp)):
+    shared_ids = set(range(E, E + n_shared))   # every token's rows: they always reach dx
+    for e in sorted(set(int(v) for v in sel_tok.reshape(-1)) | set(gexp) | shared_ids):
         wg, wu, wd = expert_f64(experts(e))
         if e >= E:                                  # shared: every token, dY = dy
             rows = np.arange(T) if e in gexp else tok

@@ -141,12 +141,14 @@ def test_uniform_bias_shift_changes_no_gradient():
     np.testing.assert_array_equal(a.dw_router, s.dw_router)
 
 
-def test_subsets_equal_full_result():
+@pytest.mark.parametrize("gexp", [[3, "shared"], [3], []])
+def test_subsets_equal_full_result(gexp):
     c, x, wr, b, ex, dy = _setup()
+    gexp = [c.E if e == "shared" else e for e in gexp]
     full = _bwd(c, x, wr, b, ex, dy)
-    sub = _bwd(c, x, wr, b, ex, dy, tokens=[2, 9], grad_experts=[3, c.E], router_cols=[5])
+    sub = _bwd(c, x, wr, b, ex, dy, tokens=[2, 9], grad_experts=gexp, router_cols=[5])
     np.testing.assert_allclose(sub.dx, full.dx[[2, 9]], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(sub.dw_router[:, 5], full.dw_router[:, 5], rtol=1e-12, atol=1e-13)
-    for e in (3, c.E):
+    for e in gexp:
         for j in range(3):
             np.testing.assert_allclose(sub.dw[e][j], full.dw[e][j], rtol=1e-12, atol=1e-13)
