@@ -194,6 +194,35 @@ int moe_balance_loss(const moe_cfg* cfg, int64_t T, int32_t seq_len, const void*
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Backward of the layer for one training step (page "02 · DeepSeek-V3",
+ * §1.3 Eq 12-15, §1.4, §2.2): the gradients of <dy, y> for the upstream
+ * gradient dy of the layer output y (the MoE branch).  The call recomputes the
+ * routing and the experts' intermediates from x (the SwiGLU output is
+ * recomputed, §2.2); the selection of experts is the forward's and carries no
+ * gradient, and the bias takes no part in backpropagation (§1.4), so it has
+ * none.  Gates are the normalised raw affinities of the chosen experts
+ * (Eq 13); their gradient flows through the normalisation and the sigmoid
+ * into x and W_r.
+ *   x, w_router, bias, w   as in moe_forward (BF16 activations and weights
+ *                          only; other dtypes return MOE_ERR_DTYPE)
+ *   dy        device bf16 [T][H] upstream gradient
+ *   dx        device bf16 [T][H] out
+ *   dw_router device float [H][E] out
+ *   dw_gate, dw_up  device float [E+S][I][H] out (experts without tokens: 0)
+ *   dw_down   device float [E+S][H][I] out
+ *   ws        workspace of at least moe_backward_workspace_bytes(cfg, T) bytes
+ * Every output is overwritten.  Sums over tokens and experts run in a fixed
+ * order (deterministic).  Staged rows use 32-bit offsets: T * (K + S) *
+ * max(H, I) * 2 must stay below 4 GiB, and H * I * 2 too (else MOE_ERR_SHAPE).
+ * T == 0 returns MOE_OK without reading pointers.
+ */
+size_t moe_backward_workspace_bytes(const moe_cfg* cfg, int64_t T);
+int moe_backward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+                 const float* bias, const moe_experts* w, const void* dy, void* dx,
+                 float* dw_router, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
  * Online activation quantisation to E4M3 (page "02 · DeepSeek-V3", §2.2: one
  * scale per 1x128 tile of a token row, from the tile's max-abs value), the
  * step moe_forward applies to x when the weights are E4M3.

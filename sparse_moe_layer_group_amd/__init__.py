@@ -18,7 +18,8 @@ import torch
 
 __all__ = ["F32", "BF16", "E4M3", "MoeError", "lib", "lib_path", "make_cfg", "cfg_from",
            "workspace_bytes", "alloc_workspace", "alloc_routing", "route", "forward",
-           "bias_update", "quantize_1x128", "balance_loss", "profile_enable", "profile_read",
+           "bias_update", "quantize_1x128", "balance_loss", "backward", "backward_workspace_bytes",
+           "alloc_backward_workspace", "profile_enable", "profile_read",
            "status_string", "abi_version", "EXPORTED_SYMBOLS"]
 
 F32, BF16, E4M3 = 0, 1, 2
@@ -28,7 +29,7 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8}
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_bias_update",
                     "moe_profile_enable", "moe_profile_read", "moe_profile_kernel_name",
                     "moe_status_string", "moe_abi_version", "moe_quantize_1x128",
-                    "moe_balance_loss")
+                    "moe_balance_loss", "moe_backward", "moe_backward_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -93,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.moe_balance_loss.argtypes = [ctypes.POINTER(_Cfg), I64, ctypes.c_int32, P, P,
                                        ctypes.c_float, P, P, P, P, SZ, P]
         L.moe_balance_loss.restype = I32
+        L.moe_backward_workspace_bytes.argtypes = [ctypes.POINTER(_Cfg), I64]
+        L.moe_backward_workspace_bytes.restype = SZ
+        L.moe_backward.argtypes = [ctypes.POINTER(_Cfg), I64, P, P, P, ctypes.POINTER(_Experts), P,
+                                   P, P, P, P, P, P, SZ, P]
+        L.moe_backward.restype = I32
         L.moe_quantize_1x128.argtypes = [P, I64, ctypes.c_int32, P, P, P]
         L.moe_quantize_1x128.restype = I32
         L.moe_profile_kernel_name.argtypes = [I32]
@@ -252,6 +258,47 @@ def forward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tens
                            ws.numel() if ws is not None else 0, _stream(stream))
     if rc != 0:
         raise MoeError(rc, "moe_forward")
+
+
+def backward_workspace_bytes(cfg: _Cfg, T: int) -> int:
+    """moe_backward_workspace_bytes (0: unsupported configuration)."""
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(cfg), int(T)))
+
+
+def alloc_backward_workspace(cfg: _Cfg, T: int, device) -> torch.Tensor:
+    n = backward_workspace_bytes(cfg, T)
+    if n == 0:
+        raise MoeError(-2, "moe_backward_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def backward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+             experts: Dict[str, torch.Tensor], dy: torch.Tensor, dx: torch.Tensor,
+             dw_router: torch.Tensor, dw_gate: torch.Tensor, dw_up: torch.Tensor,
+             dw_down: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """moe_backward: gradients of <dy, y> into dx, dw_router and the expert weight gradients."""
+    T = x.shape[0]
+    H, I, E, n = cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_experts + cfg.n_shared
+    adt, wdt = _TORCH_DT[cfg.act_dtype], _TORCH_DT[cfg.w_dtype]
+    for t, name in ((x, "x"), (dy, "dy"), (dx, "dx")):
+        _check(t, name, adt, (T, H))
+    _check(w_router, "w_router", torch.float32, (H, E))
+    _check(bias, "bias", torch.float32, (E,))
+    _check(experts.get("w_gate"), "w_gate", wdt, (n, I, H))
+    _check(experts.get("w_up"), "w_up", wdt, (n, I, H))
+    _check(experts.get("w_down"), "w_down", wdt, (n, H, I))
+    _check(dw_router, "dw_router", torch.float32, (H, E))
+    _check(dw_gate, "dw_gate", torch.float32, (n, I, H))
+    _check(dw_up, "dw_up", torch.float32, (n, I, H))
+    _check(dw_down, "dw_down", torch.float32, (n, H, I))
+    ex = _Experts(experts["w_gate"].data_ptr(), experts["w_up"].data_ptr(),
+                  experts["w_down"].data_ptr(), None, None, None)
+    rc = lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                            ctypes.byref(ex), _ptr(dy), _ptr(dx), _ptr(dw_router), _ptr(dw_gate),
+                            _ptr(dw_up), _ptr(dw_down), _ptr(ws),
+                            ws.numel() if ws is not None else 0, _stream(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_backward")
 
 
 def balance_loss(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, seq_len: int, alpha: float,

@@ -1,0 +1,595 @@
+// Backward of the MoE layer for one training step (bf16 path).
+//
+// Method: "02 · DeepSeek-V3: 671B 总参, 37B 激活, 14.8T token", §1.3 Eq 12-15
+// (gated combine, normalised sigmoid gates), §1.4 (the bias takes no part in
+// backpropagation) and §2.2 (the SwiGLU output is recomputed in the backward).
+// For the upstream gradient dy of the layer output, the kernels below form the
+// gradients of <dy, y> with respect to x, W_r and every expert's matrices; the
+// selection of experts is the forward's and carries no gradient.
+//
+// Row layout ("staged rows", as in the forward): routed expert e's rows are
+// rows offsets[e] .. offsets[e] + counts[e] - 1 in expert order (perm gives
+// their token ids), then the shared expert's T rows (row T*K + t is token t).
+//
+// GEMMs.  Two LDS-tiled grouped GEMMs on 32x32x16 bf16 MFMAs (128 x 128 tiles,
+// K steps of 32, four waves of 64 x 64, three LDS stages filled two steps ahead
+// by buffer_load ... lds copies):
+//   - dgrad:  out[row][n] = sum_k A[row][k] B[k][n] over an expert's rows,
+//     A = staged rows (k contiguous), B = the expert's weight matrix read along
+//     its slow dimension (dH = dY W_down; dX = dG W_gate + dU W_up);
+//   - wgrad:  out[m][n] = sum over the expert's rows r of A[r][m] B[r][n]
+//     (dW_down = dY^T H, dW_gate = dG^T X, dW_up = dU^T X), float32 out.
+// Operands whose contraction index is their slow (row) dimension are staged in
+// LDS as "k-rows" in memory order and read with ds_read_b64_tr_b16: in each
+// group of 16 lanes, source lane s addresses 4 consecutive columns of k-row
+// kb + s/4, and lane d receives k-rows kb .. kb+3 of column d.  Two such reads
+// give an MFMA operand's 8 consecutive k.
+#include <type_traits>
+
+#include "bwd.h"
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BG_M = 128, BG_N = 128, BG_K = 32, BG_NS = 3;
+constexpr int BG_NWAVE = 4, BG_NT = 64 * BG_NWAVE;
+constexpr int BG_STAGE = BG_M * BG_K + BG_K * BG_N;  // bf16 elements per stage (A then B)
+constexpr int BG_CPW = 4;                            // 1 KB copies per wave per step (A 2, B 2)
+static_assert(BG_M == 128 && BG_N == 128 && BG_K == 32, "copy layouts below assume this tile");
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// rows of 32 k (64 bytes): 16-byte chunk c of row r at position c ^ ((r/2) % 4)
+MOE_DEV int rswz(int r, int c) { return c ^ ((r >> 1) & 3); }
+// k-rows of 128 elements (256 bytes): 16-byte chunk c of k-row r at c ^ (2 (r % 4)),
+// so the four k-rows of one transposed read hit distinct banks
+MOE_DEV int kswz(int r, int c) { return c ^ ((r & 3) << 1); }
+
+MOE_DEV bf16x8 row_frag(const bf16_t* st, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(st + row * BG_K + (rswz(row, chunk) << 3));
+}
+
+// MFMA operand of column block i0 .. i0+31 over k kbase .. kbase+15 from a
+// k-row stage: lane l gets column i0 + l%32, k = kbase + 8 (l/32) .. +7
+MOE_DEV bf16x8 tr_frag(const bf16_t* st, int kbase, int i0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = i0 + 16 * (g & 1) + 4 * (s & 3);
+  v4i16 h[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int k = kbase + 8 * (g >> 1) + 4 * q + (s >> 2);
+    const bf16_t* p = st + k * BG_N + (kswz(k, col >> 3) << 3) + (col & 7);
+    h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)((__attribute__((address_space(3))) bf16_t*)p));
+  }
+  const v4i16 lo = h[0], hi = h[1];
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
+
+MOE_DEV float sigm(float v) { return 1.0f / (1.0f + expf(-v)); }
+
+// (row base, rows) of expert e in the staged layout
+MOE_DEV void expert_rows(const BwdArgs& g, int e, int& base, int& cnt) {
+  const bool shared = e >= g.E;
+  cnt = shared ? g.T : g.counts[e];
+  base = shared ? g.TK + (e - g.E) * g.T : g.offsets[e];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- dgrad GEMM
+// MODE 0: dH = dY W_down (K = hidden, N = inter); epilogue: SwiGLU backward,
+//         dG = dH * U * SiLU'(G), dU = dH * SiLU(G) from the staged G and U.
+// MODE 1: dX = dG W_gate + dU W_up (K = 2 x inter in two passes, N = hidden).
+template <int MODE>
+__global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[BG_NS * BG_STAGE];
+  const int N = MODE == 0 ? g.I : g.H;           // output columns
+  const int Kp = MODE == 0 ? g.H : g.I;          // K of one pass
+  const int n_nt = N / BG_N;
+  const int n_tasks = g.mt[g.n_exp] * n_nt;
+  const int task = blockIdx.x;
+  if (task >= n_tasks) return;  // uniform, before any barrier
+  int lo = 0, hi = g.n_exp - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.mt[mid] * n_nt <= task) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int n_mt = g.mt[e + 1] - g.mt[e];
+  const int local = task - g.mt[e] * n_nt;
+  const int nt = local / n_mt, mtile = local - nt * n_mt;
+  int row_base, cnt;
+  expert_rows(g, e, row_base, cnt);
+  const int m0 = mtile * BG_M, n0 = nt * BG_N;
+  const int rows = min(BG_M, cnt - m0);
+  const int nk1 = Kp / BG_K;
+  const int nk = MODE == 0 ? nk1 : 2 * nk1;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // A: staged rows [rows_total][Kp]; B: the expert's weights read as [Kp][N]
+  const uint32_t total_rows = uint32_t(g.TK + (g.n_exp - g.E) * g.T);
+  const bf16_t* a0p = MODE == 0 ? g.dyst : g.dgst;
+  const bf16_t* a1p = MODE == 0 ? g.dyst : g.dust;
+  const __amdgpu_buffer_rsrc_t ar0 = buffer_rsrc(a0p, total_rows * uint32_t(Kp) * 2u);
+  const __amdgpu_buffer_rsrc_t ar1 = buffer_rsrc(a1p, total_rows * uint32_t(Kp) * 2u);
+  const size_t wsz = size_t(Kp) * N;
+  const bf16_t* b0p = (MODE == 0 ? g.w_down : g.w_gate) + size_t(e) * wsz;
+  const bf16_t* b1p = (MODE == 0 ? g.w_down : g.w_up) + size_t(e) * wsz;
+  const __amdgpu_buffer_rsrc_t br0 = buffer_rsrc(b0p, uint32_t(wsz * 2));
+  const __amdgpu_buffer_rsrc_t br1 = buffer_rsrc(b1p, uint32_t(wsz * 2));
+
+  // copy sources: A copy i of wave w covers tile rows 16 (2w+i) .. +15 (lane
+  // l: row + l/4, position l%4); B copy i covers k-rows 4 (2w+i) .. +3 (lane l:
+  // k-row + l/16, position l%16)
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (2 * wave + i) + (lane >> 2);
+    const int m = row_base + m0 + min(r, rows - 1);  // rows past the count re-read a valid row
+    aoff[i] = (uint32_t(m) * uint32_t(Kp) + uint32_t(rswz(r, lane & 3) * 8)) * 2u;
+    const int kr = 4 * (2 * wave + i) + (lane >> 4);
+    boff[i] = (uint32_t(kr) * uint32_t(N) + uint32_t(n0 + kswz(kr, lane & 15) * 8)) * 2u;
+  }
+  auto copy_step = [&](int kt) {
+    const int k = min(kt, nk - 1);
+    const bool second = MODE == 1 && k >= nk1;
+    const int kk = second ? k - nk1 : k;
+    bf16_t* st = smem + (kt % BG_NS) * BG_STAGE;
+    const __amdgpu_buffer_rsrc_t ar = second ? ar1 : ar0;
+    const __amdgpu_buffer_rsrc_t br = second ? br1 : br0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      copy16_to_lds(ar, aoff[i] + uint32_t(kk * BG_K * 2), st + 16 * (2 * wave + i) * BG_K);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      copy16_to_lds(br, boff[i] + uint32_t(kk * BG_K) * uint32_t(N) * 2u,
+                    st + BG_M * BG_K + 4 * (2 * wave + i) * BG_N);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  copy_step(0);
+  copy_step(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(BG_CPW));  // this wave's copies of kt landed
+    __builtin_amdgcn_s_barrier();
+    copy_step(kt + 2);
+    const bf16_t* st = smem + (kt % BG_NS) * BG_STAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = row_frag(st, wm * 64 + 32 * i + (lane & 31), 2 * s + (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = tr_frag(st + BG_M * BG_K, 16 * s, wn * 64 + 32 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  // epilogue.  32x32 accumulator v of lane l: row 8 (v/4) + 4 (l/32) + v%4, column l%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r >= rows) continue;
+        const size_t o = size_t(row_base + m0 + r) * N + col;
+        const float d = acc[i][j][v];
+        if (MODE == 0) {
+          const float G = bf16_to_f32(g.gst[o]), U = bf16_to_f32(g.ust[o]);
+          const float sg = sigm(G);
+          g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
+          g.dust[o] = f32_to_bf16(d * G * sg);
+        } else {
+          g.dxst[o] = f32_to_bf16(d);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------- wgrad GEMM
+// out[e][m][n] = sum over expert e's rows r of A[r][m] B[r][n], float32.
+// MODE 0: dW_down (A = dY [.][hidden], B = H [.][inter]);
+// MODE 1: dW_gate (A = dG [.][inter], B = X [.][hidden]); MODE 2: dW_up (A = dU).
+template <int MODE>
+__global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[BG_NS * 2 * BG_K * BG_N];
+  constexpr int STG = 2 * BG_K * BG_N;           // A k-rows then B k-rows
+  const int M = MODE == 0 ? g.H : g.I;
+  const int N = MODE == 0 ? g.I : g.H;
+  const int tm = M / BG_M, tn = N / BG_N;
+  const int e = blockIdx.x / (tm * tn);
+  if (e >= g.n_exp) return;  // uniform
+  const int t = blockIdx.x - e * tm * tn;
+  const int mt = t / tn, ntile = t - mt * tn;
+  const int m0 = mt * BG_M, n0 = ntile * BG_N;
+  int row_base, cnt;
+  expert_rows(g, e, row_base, cnt);
+  const int nk = (cnt + BG_K - 1) / BG_K;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const uint32_t total_rows = uint32_t(g.TK + (g.n_exp - g.E) * g.T);
+  const bf16_t* ap = MODE == 0 ? g.dyst : (MODE == 1 ? g.dgst : g.dust);
+  const bf16_t* bp = MODE == 0 ? g.hst : g.xst;
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(ap, total_rows * uint32_t(M) * 2u);
+  const __amdgpu_buffer_rsrc_t br = buffer_rsrc(bp, total_rows * uint32_t(N) * 2u);
+  // copy i of wave w covers k-rows 4 (2w+i) .. +3 of the step (lane l: + l/16,
+  // position l%16); k-rows past the expert's rows read beyond the buffer, which
+  // returns zeros
+  uint32_t acol[2], bcol[2];
+  int krow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    krow[i] = 4 * (2 * wave + i) + (lane >> 4);
+    acol[i] = uint32_t(m0 + kswz(krow[i], lane & 15) * 8);
+    bcol[i] = uint32_t(n0 + kswz(krow[i], lane & 15) * 8);
+  }
+  auto copy_step = [&](int kt) {
+    const int k = min(kt, max(nk - 1, 0));
+    bf16_t* st = smem + (kt % BG_NS) * STG;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = k * BG_K + krow[i];
+      const bool ok = r < cnt;
+      const uint32_t row = uint32_t(row_base + r);
+      const uint32_t ao = ok ? (row * uint32_t(M) + acol[i]) * 2u : 0xfffffff0u;
+      const uint32_t bo = ok ? (row * uint32_t(N) + bcol[i]) * 2u : 0xfffffff0u;
+      copy16_to_lds(ar, ao, st + 4 * (2 * wave + i) * BG_N);
+      copy16_to_lds(br, bo, st + BG_K * BG_N + 4 * (2 * wave + i) * BG_N);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  if (nk > 0) {  // uniform
+    copy_step(0);
+    copy_step(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(BG_CPW));
+      __builtin_amdgcn_s_barrier();
+      copy_step(kt + 2);
+      const bf16_t* st = smem + (kt % BG_NS) * STG;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 af[2], bf[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[i] = tr_frag(st, 16 * s, wm * 64 + 32 * i, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = tr_frag(st + BG_K * BG_N, 16 * s, wn * 64 + 32 * j, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+  }
+
+  float* out = (MODE == 0 ? g.dw_down : (MODE == 1 ? g.dw_gate : g.dw_up)) + size_t(e) * M * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        out[size_t(r) * N + col] = acc[i][j][v];
+      }
+    }
+}
+
+// ---------------------------------------------------------------- row kernels
+
+// Xst[r] = x[perm[r]] (routed rows), Xst[T K + t] = x[t] (shared rows)
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm, int T,
+                                                          int TK, int S, int H,
+                                                          bf16_t* __restrict__ xst) {
+  const int r = blockIdx.x;
+  const int src = r < TK ? perm[r] : (r - TK) % T;
+  const u32x4* s = reinterpret_cast<const u32x4*>(x + size_t(src) * H);
+  u32x4* d = reinterpret_cast<u32x4*>(xst + size_t(r) * H);
+  for (int c = threadIdx.x; c < H / 8; c += 256) d[c] = s[c];
+}
+
+// H = SiLU(G) * U, elementwise over the staged rows
+__global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ gst,
+                                                     const bf16_t* __restrict__ ust, long long n,
+                                                     bf16_t* __restrict__ hst) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float G = bf16_to_f32(gst[i]), U = bf16_to_f32(ust[i]);
+  hst[i] = f32_to_bf16(G * sigm(G) * U);
+}
+
+// Per token t: for each chosen expert k, the gate gradient dg = <dy_t, Y_k[t]>
+// (fixed-order block reduction) and the expert's output gradient g_k dy_t; the
+// shared expert's output gradient is dy_t itself.
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dy,
+                                                          const bf16_t* __restrict__ yst,
+                                                          const int32_t* __restrict__ slot,
+                                                          const float* __restrict__ gate, int T,
+                                                          int K, int H, int TK, int S,
+                                                          bf16_t* __restrict__ dyst,
+                                                          float* __restrict__ dg) {
+  __shared__ float red[32][4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = H / 8;
+  const u32x4* d8 = reinterpret_cast<const u32x4*>(dy + size_t(t) * H);
+  if (S > 0) {
+    u32x4* o = reinterpret_cast<u32x4*>(dyst + size_t(TK + t) * H);
+    for (int c = tid; c < nch; c += 256) o[c] = d8[c];
+  }
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const int kn = min(32, K - k0);
+    float part[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) part[k] = 0.f;
+    for (int c = tid; c < nch; c += 256) {
+      const u32x4 dv = d8[c];
+      float dyf[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dyf[2 * q] = __uint_as_float(dv[q] << 16);
+        dyf[2 * q + 1] = __uint_as_float(dv[q] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        if (k >= kn) continue;  // uniform
+        const int sl = slot[t * K + k0 + k];
+        const float gk = gate[t * K + k0 + k];
+        const u32x4 yv = reinterpret_cast<const u32x4*>(yst + size_t(sl) * H)[c];
+        u32x4 ov;
+        float p = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float y0 = __uint_as_float(yv[q] << 16), y1 = __uint_as_float(yv[q] & 0xffff0000u);
+          p = fmaf(dyf[2 * q], y0, p);
+          p = fmaf(dyf[2 * q + 1], y1, p);
+          ov[q] = uint32_t(f32_to_bf16(gk * dyf[2 * q])) |
+                  (uint32_t(f32_to_bf16(gk * dyf[2 * q + 1])) << 16);
+        }
+        part[k] += p;
+        reinterpret_cast<u32x4*>(dyst + size_t(sl) * H)[c] = ov;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k >= kn) continue;  // uniform
+      const float w = wave_sum(part[k]);
+      if (lane == 0) red[k][wave] = w;
+    }
+    __syncthreads();
+    if (tid < kn) dg[t * K + k0 + tid] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3];
+    __syncthreads();
+  }
+}
+
+// Per token: affinities of the chosen experts from the router partials (added
+// in partial order, as the selection does), gate normalisation and sigmoid
+// backward: ds_k = (dg_k - sum_j dg_j g_j) / S, dL_k = ds_k s_k (1 - s_k).
+// Writes dL per assignment [T][K] and per staged row.
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ P, int ks,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ slot,
+                                                         const float* __restrict__ dg, int T,
+                                                         int E, int K, float* __restrict__ dl,
+                                                         float* __restrict__ dlst) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  float s[32];
+  float S = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int e = idx[t * K + k];
+    float L = 0.f;
+    for (int c = 0; c < ks; ++c) L += P[(size_t(c) * T + t) * E + e];
+    s[k] = sigm(L);
+    S += s[k];
+  }
+  float dsum = 0.f;
+  for (int k = 0; k < K; ++k) dsum += dg[t * K + k] * (s[k] / S);
+  for (int k = 0; k < K; ++k) {
+    const float v = (dg[t * K + k] - dsum) / S * s[k] * (1.0f - s[k]);
+    dl[t * K + k] = v;
+    dlst[slot[t * K + k]] = v;
+  }
+}
+
+// dW_r^T[e][h] = sum over expert e's routed rows r of dL_r X_r[h], rows in order
+__global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dlst,
+                                                  const bf16_t* __restrict__ xst,
+                                                  const int32_t* __restrict__ counts,
+                                                  const int32_t* __restrict__ offsets, int H,
+                                                  float* __restrict__ dwrt) {
+  const int e = blockIdx.x;
+  const int h = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (h >= H) return;
+  const int base = offsets[e], cnt = counts[e];
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int r = 0; r < cnt; ++r) {
+    const float w = dlst[base + r];
+    const uint2 v = *reinterpret_cast<const uint2*>(xst + size_t(base + r) * H + h);
+    a0 = fmaf(w, __uint_as_float(v.x << 16), a0);
+    a1 = fmaf(w, __uint_as_float(v.x & 0xffff0000u), a1);
+    a2 = fmaf(w, __uint_as_float(v.y << 16), a2);
+    a3 = fmaf(w, __uint_as_float(v.y & 0xffff0000u), a3);
+  }
+  *reinterpret_cast<f32x4*>(dwrt + size_t(e) * H + h) = f32x4{a0, a1, a2, a3};
+}
+
+// out[c][r] = in[r][c], float32, through a 32 x 33 LDS tile
+__global__ __launch_bounds__(256) void transpose_f32_kernel(const float* __restrict__ in, int R,
+                                                            int C, float* __restrict__ out) {
+  __shared__ float tile[32][33];
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 8 rows per pass
+  for (int i = ty; i < 32; i += 8)
+    if (r0 + i < R && c0 + tx < C) tile[i][tx] = in[size_t(r0 + i) * C + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8)
+    if (c0 + i < C && r0 + tx < R) out[size_t(c0 + i) * R + r0 + tx] = tile[tx][i];
+}
+
+// dx_t = dX_shared[t] + sum_k dX[slot(t, k)] + sum_k dL_tk W_r[:, e_k], float32
+// in that order, bf16 out
+__global__ __launch_bounds__(256) void dx_kernel(const bf16_t* __restrict__ dxst,
+                                                 const int32_t* __restrict__ slot,
+                                                 const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ dl,
+                                                 const float* __restrict__ wrt, int T, int K,
+                                                 int H, int TK, int S, bf16_t* __restrict__ dx) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    float a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = 0.f;
+    auto add_row = [&](size_t row) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(dxst + row * H)[c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[2 * q] += __uint_as_float(v[q] << 16);
+        a[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+      }
+    };
+    if (S > 0) add_row(size_t(TK + t));
+    for (int k = 0; k < K; ++k) add_row(size_t(slot[t * K + k]));
+    for (int k = 0; k < K; ++k) {
+      const float w = dl[t * K + k];
+      const f32x4* r = reinterpret_cast<const f32x4*>(wrt + size_t(idx[t * K + k]) * H + 8 * c);
+      const f32x4 r0 = r[0], r1 = r[1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = fmaf(w, r0[q], a[q]);
+        a[4 + q] = fmaf(w, r1[q], a[4 + q]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = uint32_t(f32_to_bf16(a[2 * q])) | (uint32_t(f32_to_bf16(a[2 * q + 1])) << 16);
+    reinterpret_cast<u32x4*>(dx + size_t(t) * H)[c] = o;
+  }
+}
+
+// row-tile prefix of the dgrad GEMM: mt[e] = sum over experts before e of
+// ceil(rows / 128) (routed counts, then the shared experts' T rows)
+__global__ __launch_bounds__(64) void bwd_tile_prefix_kernel(const int32_t* __restrict__ counts,
+                                                             int E, int S, int T,
+                                                             int32_t* __restrict__ mt) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int e = 0; e < E + S; ++e) {
+    mt[e] = acc;
+    const int c = e < E ? counts[e] : T;
+    acc += (c + BG_M - 1) / BG_M;
+  }
+  mt[E + S] = acc;
+}
+
+// ---------------------------------------------------------------- launches
+
+int bwd_max_row_tiles(int T, int K, int E, int S) {
+  return (T * K + BG_M - 1) / BG_M + E + S * ((T + BG_M - 1) / BG_M);
+}
+
+hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, const int32_t* idx,
+                                   const int32_t* slot, const float* gate, const float* w_router,
+                                   const bf16_t* dy, bf16_t* dx, float* dw_router, hipStream_t st,
+                                   int stage) {
+  const int T = g.T, K = g.K, E = g.E, S = g.n_exp - g.E, H = g.H, I = g.I;
+  const int rows = g.TK + S * T;
+  switch (stage) {
+    case 0:  // expert-ordered copy of x
+      hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(256), 0, st, g.x, g.perm, T, g.TK, S,
+                         H, g.xst);
+      break;
+    case 1:  // H from the recomputed G and U
+      hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned((size_t(rows) * I + 255) / 256)), dim3(256),
+                         0, st, g.gst, g.ust, (long long)rows * I, g.hst);
+      break;
+    case 2:  // combine backward
+      hipLaunchKernelGGL(combine_bwd_kernel, dim3(T), dim3(256), 0, st, dy, g.yst, slot, gate, T, K,
+                         H, g.TK, S, g.dyst, g.dg);
+      break;
+    case 3:  // router backward and the dgrad row-tile prefix
+      hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 255) / 256), dim3(256), 0, st, P, ks, idx,
+                         slot, g.dg, T, E, K, g.dl, g.dlst);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(bwd_tile_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T,
+                         const_cast<int32_t*>(g.mt));
+      break;
+    case 4:  // dH = dY W_down with the SwiGLU backward
+      hipLaunchKernelGGL(dgrad_gemm_kernel<0>, dim3(unsigned(bwd_max_row_tiles(T, K, E, S) * (I / BG_N))),
+                         dim3(BG_NT), 0, st, g);
+      break;
+    case 5:  // dX = dG W_gate + dU W_up
+      hipLaunchKernelGGL(dgrad_gemm_kernel<1>, dim3(unsigned(bwd_max_row_tiles(T, K, E, S) * (H / BG_N))),
+                         dim3(BG_NT), 0, st, g);
+      break;
+    case 6: {  // weight gradients
+      const unsigned tiles = unsigned((H / BG_M) * (I / BG_N) * (E + S));
+      hipLaunchKernelGGL(wgrad_gemm_kernel<0>, dim3(tiles), dim3(BG_NT), 0, st, g);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(wgrad_gemm_kernel<1>, dim3(tiles), dim3(BG_NT), 0, st, g);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(wgrad_gemm_kernel<2>, dim3(tiles), dim3(BG_NT), 0, st, g);
+      break;
+    }
+    case 7:  // router weight gradient: dW_r^T per expert, then transposed
+      hipLaunchKernelGGL(dwr_kernel, dim3(E, (H / 4 + 255) / 256), dim3(256), 0, st, g.dlst, g.xst,
+                         g.counts, g.offsets, H, g.dwrt);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(transpose_f32_kernel, dim3((H + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
+                         g.dwrt, E, H, dw_router);
+      break;
+    case 8:  // dx: W_r^T, then the fixed-order gather
+      hipLaunchKernelGGL(transpose_f32_kernel, dim3((E + 31) / 32, (H + 31) / 32), dim3(256), 0, st,
+                         w_router, H, E, g.wrt);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(dx_kernel, dim3(T), dim3(256), 0, st, g.dxst, slot, idx, g.dl, g.wrt, T, K,
+                         H, g.TK, S, dx);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/moe.h"
+#include "bwd.h"
 #include "kernels.h"
 
 namespace {
@@ -134,11 +135,13 @@ int check_device() {
 
 enum Slot {
   K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_QUANT, K_BAL,
+  K_BWD_RECOMPUTE, K_BWD_COMBINE, K_BWD_DH, K_BWD_DX, K_BWD_WGRAD, K_BWD_ROUTER,
   K_NSLOTS
 };
-const char* const kSlotNames[K_NSLOTS] = {"router_logits", "select",      "permute",
-                                          "gemm_gate_up",  "gemm_down",   "combine",
-                                          "bias_update",   "quantize",    "balance_loss"};
+const char* const kSlotNames[K_NSLOTS] = {
+    "router_logits", "select",        "permute",       "gemm_gate_up",  "gemm_down",
+    "combine",       "bias_update",   "quantize",      "balance_loss",  "bwd_recompute",
+    "bwd_combine",   "bwd_dgrad_down", "bwd_dgrad_gate_up", "bwd_wgrad", "bwd_router_dx"};
 
 struct Prof {
   bool on = false;
@@ -361,6 +364,151 @@ int run_experts_fp8(const moe_cfg& c, int T, const bf16_t* x, const moe_experts*
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- backward
+
+// Workspace of the backward: the forward's layout (routing, H and Y staging),
+// then the backward's staged rows and per-assignment buffers.
+struct BwdLayout {
+  Layout f;
+  size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dl, dlst, wrt, dwrt, mt, total;
+};
+
+BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
+  BwdLayout B{};
+  B.f = make_layout(c, T);
+  size_t off = B.f.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
+  const size_t TK = size_t(T) * K, rows = TK + S * size_t(T);
+  B.xst = take(rows * H * 2);
+  B.gst = take(rows * I * 2);
+  B.ust = take(rows * I * 2);
+  B.dyst = take(rows * H * 2);
+  B.dgst = take(rows * I * 2);
+  B.dust = take(rows * I * 2);
+  B.dxst = take(rows * H * 2);
+  B.dg = take(TK * 4);
+  B.dl = take(TK * 4);
+  B.dlst = take(TK * 4);
+  B.wrt = take(E * H * 4);
+  B.dwrt = take(E * H * 4);
+  B.mt = take((E + S + 1) * 4);
+  B.total = off;
+  return B;
+}
+
+// The backward stages its rows with 32-bit byte offsets: every staged-row
+// buffer must span less than 4 GiB.
+int validate_bwd(const moe_cfg* c, int64_t T) {
+  if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  const int64_t rows = T * int64_t(c->topk + c->n_shared);
+  if (rows * std::max<int64_t>(c->hidden, c->inter) * 2 >= (int64_t(1) << 32) - 256) return MOE_ERR_SHAPE;
+  if (int64_t(c->hidden) * c->inter * 2 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// plain (non-gated) expert GEMM on staged rows, out[row][n] = sum_k a[row][k] w[e][n][k],
+// dispatched like the forward's down GEMM
+int run_plain_gemm(const moe_cfg& c, int T, const bf16_t* a, const bf16_t* w, bf16_t* out, int N,
+                   int Kd, const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, S = c.n_shared;
+  const int TK = T * K;
+  const int bm = tile_rows(c);
+  const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
+  const int smax = stream_max_rows(c, T);
+  const bool streams = smax >= 0, tiles = smax < T;
+  if (streams) {
+    const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
+    const long long waves = chunks * (N / 128);
+    const int blocks =
+        int(std::max<long long>(1, std::min<long long>((waves + 3) / 4, (long long)cu_count())));
+    moe::StreamArgs sa{a, w, nullptr, out, r.perm, r.counts, r.offsets,
+                       at<int32_t>(ws, L.chunk_start), E, E + S, T, TK, N, Kd};
+    hipError_t err = moe::launch_stream_gemm(sa, false, blocks, st);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    if (!tiles) return MOE_OK;
+  }
+  moe::TileArgs ta{a, w, nullptr, out, r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_start),
+                   E, E + S, T, TK, N, Kd};
+  return moe::launch_tile_gemm(ta, false, max_mt, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, const float* bias,
+                 const moe_experts* w, const bf16_t* dy, bf16_t* dx, float* dwr, float* dwg,
+                 float* dwu, float* dwd, void* ws, const BwdLayout& B, hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
+  const Layout& L = B.f;
+  const RoutePtrs r = route_ptrs(nullptr, ws, L);
+  int rc = run_route(c, T, x, wr, bias, r, ws, L, st);
+  if (rc != MOE_OK) return rc;
+  moe::BwdArgs g{};
+  g.x = x;
+  g.perm = r.perm;
+  g.counts = r.counts;
+  g.offsets = r.offsets;
+  g.mt = at<int32_t>(ws, B.mt);
+  g.w_gate = static_cast<const bf16_t*>(w->w_gate);
+  g.w_up = static_cast<const bf16_t*>(w->w_up);
+  g.w_down = static_cast<const bf16_t*>(w->w_down);
+  g.xst = at<bf16_t>(ws, B.xst);
+  g.gst = at<bf16_t>(ws, B.gst);
+  g.ust = at<bf16_t>(ws, B.ust);
+  g.hst = at<bf16_t>(ws, L.hst);
+  g.yst = at<bf16_t>(ws, L.yst);
+  g.dyst = at<bf16_t>(ws, B.dyst);
+  g.dgst = at<bf16_t>(ws, B.dgst);
+  g.dust = at<bf16_t>(ws, B.dust);
+  g.dxst = at<bf16_t>(ws, B.dxst);
+  g.dg = at<float>(ws, B.dg);
+  g.dl = at<float>(ws, B.dl);
+  g.dlst = at<float>(ws, B.dlst);
+  g.wrt = at<float>(ws, B.wrt);
+  g.dwrt = at<float>(ws, B.dwrt);
+  g.dw_gate = dwg;
+  g.dw_up = dwu;
+  g.dw_down = dwd;
+  g.E = E;
+  g.n_exp = E + S;
+  g.T = T;
+  g.TK = T * K;
+  g.K = K;
+  g.H = H;
+  g.I = I;
+  const float* P = at<float>(ws, L.P);
+  const int ks = moe::router_partials(T, H, E, true);
+  auto stage = [&](int s) {
+    return moe::launch_backward_kernels(g, P, ks, r.idx, r.slot, r.gate, wr, dy, dx, dwr, st, s);
+  };
+  // recompute the forward's expert intermediates from x (G, U, H and Y)
+  MOE_TRY(timed(K_BWD_RECOMPUTE, st, [&]() -> hipError_t {
+    hipError_t err = stage(0);
+    if (err != hipSuccess) return err;
+    if (run_plain_gemm(c, T, g.xst, g.w_gate, g.gst, I, H, r, ws, L, st) != MOE_OK ||
+        run_plain_gemm(c, T, g.xst, g.w_up, g.ust, I, H, r, ws, L, st) != MOE_OK)
+      return hipErrorLaunchFailure;
+    if ((err = stage(1)) != hipSuccess) return err;
+    if (run_plain_gemm(c, T, g.hst, g.w_down, g.yst, H, I, r, ws, L, st) != MOE_OK)
+      return hipErrorLaunchFailure;
+    return hipSuccess;
+  }));
+  MOE_TRY(timed(K_BWD_COMBINE, st, [&]() -> hipError_t {
+    hipError_t err = stage(2);
+    return err != hipSuccess ? err : stage(3);
+  }));
+  MOE_TRY(timed(K_BWD_DH, st, [&] { return stage(4); }));
+  MOE_TRY(timed(K_BWD_DX, st, [&] { return stage(5); }));
+  MOE_TRY(timed(K_BWD_WGRAD, st, [&] { return stage(6); }));
+  MOE_TRY(timed(K_BWD_ROUTER, st, [&]() -> hipError_t {
+    hipError_t err = stage(7);
+    return err != hipSuccess ? err : stage(8);
+  }));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -465,6 +613,34 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   return run_experts<float>(*cfg, int(T), static_cast<const float*>(x), w,
                             static_cast<const float*>(residual), static_cast<float*>(y), r, ws, L,
                             st);
+}
+
+size_t moe_backward_workspace_bytes(const moe_cfg* cfg, int64_t T) {
+  if (validate_cfg(cfg) != MOE_OK || validate_T(cfg, T) != MOE_OK || validate_bwd(cfg, T) != MOE_OK)
+    return 0;
+  return make_bwd_layout(*cfg, T).total;
+}
+
+int moe_backward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+                 const float* bias, const moe_experts* w, const void* dy, void* dx,
+                 float* dw_router, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if ((rc = validate_bwd(cfg, T)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || bias == nullptr || w == nullptr || dy == nullptr ||
+      dx == nullptr || dw_router == nullptr || dw_gate == nullptr || dw_up == nullptr ||
+      dw_down == nullptr)
+    return MOE_ERR_NULL;
+  if (w->w_gate == nullptr || w->w_up == nullptr || w->w_down == nullptr) return MOE_ERR_NULL;
+  const BwdLayout B = make_bwd_layout(*cfg, T);
+  if (ws == nullptr || ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  if ((rc = check_device()) != MOE_OK) return rc;
+  return run_backward(*cfg, int(T), static_cast<const bf16_t*>(x), w_router, bias, w,
+                      static_cast<const bf16_t*>(dy), static_cast<bf16_t*>(dx), dw_router, dw_gate,
+                      dw_up, dw_down, ws, B, static_cast<hipStream_t>(stream));
 }
 
 int moe_quantize_1x128(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,

@@ -185,3 +185,29 @@ def test_balance_loss_argument_checks():
                               None, one, ctypes.c_size_t(100), None) == -4
     assert L.moe_balance_loss(ctypes.byref(c), 0, 1, None, None, ctypes.c_float(1e-4), None, None,
                               None, None, ctypes.c_size_t(0), None) == 0
+
+
+def test_backward_argument_checks():
+    L = moe.lib()
+    c = _v3()
+    one = ctypes.c_void_p(1)
+    ex = moe._Experts(1, 1, 1, None, None, None)
+    big = ctypes.c_size_t(1 << 40)
+    n = L.moe_backward_workspace_bytes(ctypes.byref(c), 8192)
+    assert n > L.moe_workspace_bytes(ctypes.byref(c), 8192) > 0
+    # bf16 activations and weights only
+    for kw in (dict(act_dtype=moe.F32, w_dtype=moe.F32), dict(w_dtype=moe.E4M3)):
+        cc = _v3(**kw)
+        assert L.moe_backward_workspace_bytes(ctypes.byref(cc), 256) == 0
+        assert L.moe_backward(ctypes.byref(cc), 256, one, one, one, ctypes.byref(ex), one, one, one,
+                              one, one, one, one, big, None) == -3
+    # staged rows past 4 GiB of 32-bit offsets
+    assert L.moe_backward(ctypes.byref(c), 40000, one, one, one, ctypes.byref(ex), one, one, one,
+                          one, one, one, one, big, None) == -2
+    # missing outputs, small workspace, zero tokens
+    assert L.moe_backward(ctypes.byref(c), 256, one, one, one, ctypes.byref(ex), one, one, None,
+                          one, one, one, one, big, None) == -1
+    assert L.moe_backward(ctypes.byref(c), 256, one, one, one, ctypes.byref(ex), one, one, one,
+                          one, one, one, one, ctypes.c_size_t(100), None) == -4
+    assert L.moe_backward(ctypes.byref(c), 0, None, None, None, None, None, None, None, None,
+                          None, None, None, ctypes.c_size_t(0), None) == 0
