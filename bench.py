@@ -129,7 +129,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "fp8"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skew", "fp8", "backward"])
+    ap.add_argument("--backward-shape", default="prefill", choices=["decode", "prefill"],
+                    help="backward workload: batch shape (prefill T=8192 or decode T=256)")
     ap.add_argument("--skew-steps", type=int, default=200,
                     help="skew workload: bias-update steps (forward timed at first, middle, last)")
     ap.add_argument("--cpu-tokens", type=int, default=32,
@@ -154,6 +157,10 @@ def main():
 
     import sparse_moe_layer_group_amd as moe
     import synthetic as S
+
+    if args.workload == "backward":
+        bench_backward(args, np, torch, moe, S)
+        return
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
@@ -307,6 +314,120 @@ def main():
         **({"skew": skew} if skew is not None else {}),
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_backward(args, np, torch, moe, S):
+    """Layer backward for one training step (moe_backward) on a V3-shape batch:
+    tokens/s of the backward, and the roofline of its dominant kernel, the
+    weight-gradient GEMMs (float32 gradients of all 257 experts' matrices)."""
+    dev = torch.device("cuda:0")
+    c = S.get_config(args.backward_shape)
+    cfg = moe.cfg_from(c)
+    T, H, I, E, K, Sn = c.T, c.hidden, c.inter, c.n_experts, c.topk, c.n_shared
+    n = E + Sn
+    log(f"backward on the {c.name} batch: T={T}; generating inputs on the GPU")
+    x = S.gen_x(c, device=dev)
+    wr = S.gen_router(c, device=dev)
+    b = S.gen_bias(c, device=dev)
+    ex = S.gen_experts(c, device=dev)
+    g = torch.Generator().manual_seed(99)
+    dy_cpu = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    dy = dy_cpu.to(dev)
+    dx = torch.empty_like(x)
+    dwr = torch.empty((H, E), dtype=torch.float32, device=dev)
+    dwg = torch.empty((n, I, H), dtype=torch.float32, device=dev)
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((n, H, I), dtype=torch.float32, device=dev)
+    ws = moe.alloc_backward_workspace(cfg, T, dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        moe.backward(cfg, x, wr, b, ex, dy, dx, dwr, dwg, dwu, dwd, ws, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    moe.profile_read()
+    moe.profile_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    moe.profile_enable(False)
+    kern = moe.profile_read()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} backward steps: {ms:.4f} ms/step")
+    for k, (kms, nn) in kern.items():
+        if nn:
+            log(f"  {k:18s} {kms / nn * 1e3:9.1f} us/call  ({nn} calls)")
+
+    rows = T * K + Sn * T
+    # weight-gradient GEMMs (one call = three launches: dW_down, dW_gate, dW_up):
+    # float32 gradients of every expert written once, staged operands read once
+    # per launch (dY and H; dG and X; dU and X)
+    wg_ms, wg_n = kern["bwd_wgrad"]
+    wg_s = wg_ms / max(wg_n, 1) / 1e3
+    wg_bytes = n * 3 * H * I * 4 + rows * (3 * H + 3 * I) * 2
+    wg_flops = 3 * 2 * rows * H * I
+    roofline = {"bound": "hbm", "achieved": round(wg_bytes / wg_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(wg_bytes / wg_s / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": None, "kernel": "bwd_wgrad (dW_down, dW_gate, dW_up launches)",
+                "kernel_us": round(wg_s * 1e6, 2), "alg_bytes_per_launch": int(wg_bytes),
+                "alg_flops_per_launch": int(wg_flops),
+                "mfma_frac": round(wg_flops / wg_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+    # the whole backward: expert recompute, dgrad and wgrad (3 x the forward's
+    # expert flops) plus the router's; weights read twice, gradients written
+    bw_flops = 3 * rows * 2 * 3 * H * I + 2 * T * K * H * 2
+    bw_bytes = 2 * n * 3 * H * I * 2 + n * 3 * H * I * 4 + 3 * T * H * 2 + 2 * H * E * 4
+    backward = {"ms": round(ms, 4), "alg_bytes": int(bw_bytes), "alg_flops": int(bw_flops),
+                "hbm_frac": round(bw_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(bw_flops / (ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                "kernels_us": {k: round(v / nn * 1e3, 1) for k, (v, nn) in kern.items() if nn}}
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline_backward(c, min(args.cpu_tokens, 4), x, b, dy_cpu)
+    res = {
+        "metric": "MoE-layer backward tokens/s on 1 MI355X (one training step's layer gradients)",
+        "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 inputs and upstream gradient, V3 layer shapes)",
+        "config": {"workload": f"backward on the {c.name} batch: DeepSeek-V3 MoE layer gradients "
+                               f"(dx, dW_r, dW of 257 experts in float32), T={T}, hidden {H}, "
+                               f"inter {I}, {E} routed + {Sn} shared, top-{K}, bf16",
+                   "T": T, "hidden": H, "inter": I, "n_experts": E, "n_shared": Sn, "topk": K},
+        "roofline": roofline, "backward": backward, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_backward(c, n_tok, x_dev, b_dev, dy_cpu):
+    """The oracle's backward (float64, as it stands) on the first n_tok tokens
+    of the batch as a batch of their own, with the weight gradients of every
+    expert they touch and of the shared expert; input generation excluded."""
+    import numpy as np
+    import oracle as O
+    import synthetic as S
+    x = O.lift(x_dev[:n_tok].float().cpu())
+    wr = O.lift(S.gen_router(c, "cpu"))
+    b = b_dev.cpu().numpy()
+    dy = O.lift(dy_cpu[:n_tok].float())
+    L, s, r, p = O.route(x, wr, b, n_groups=c.n_groups, topk_groups=c.topk_groups, topk=c.topk,
+                         group_topn=c.group_topn)
+    touched = sorted(set(int(v) for v in r.idx.reshape(-1))) + list(range(c.n_experts, c.n_experts + c.n_shared))
+    cache = {e: S.gen_expert(c, e, "cpu") for e in touched}
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    O.backward(x, wr, b, lambda e: cache[e], dy, n_groups=c.n_groups, topk_groups=c.topk_groups,
+               topk=c.topk, group_topn=c.group_topn, n_shared=c.n_shared, grad_experts=touched)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: oracle backward of {n_tok} tokens ({len(touched)} experts' gradients) "
+        f"in {dt:.1f}s on {cores} cores")
+    return {"value": round(n_tok / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle backward of the first {n_tok} tokens as their own batch "
+                      f"(dx, dW_r, and dW of the {len(touched)} experts they touch, shared included)"}
 
 
 def router_partials(T, H, E):
