@@ -204,7 +204,8 @@ int moe_balance_loss(const moe_cfg* cfg, int64_t T, int32_t seq_len, const void*
  * (Eq 13); their gradient flows through the normalisation and the sigmoid
  * into x and W_r.
  *   x, w_router, bias, w   as in moe_forward (BF16 activations and weights
- *                          only; other dtypes return MOE_ERR_DTYPE)
+ *                          only; other dtypes return MOE_ERR_DTYPE; hidden
+ *                          and inter multiples of 256, else MOE_ERR_SHAPE)
  *   dy        device bf16 [T][H] upstream gradient
  *   dx        device bf16 [T][H] out
  *   dw_router device float [H][E] out

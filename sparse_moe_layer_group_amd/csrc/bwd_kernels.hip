@@ -53,7 +53,8 @@ MOE_DEV bf16x8 row_frag(const bf16_t* st, int row, int chunk) {
 }
 
 // MFMA operand of column block i0 .. i0+31 over k kbase .. kbase+15 from a
-// k-row stage: lane l gets column i0 + l%32, k = kbase + 8 (l/32) .. +7
+// k-row stage of RL columns: lane l gets column i0 + l%32, k = kbase + 8 (l/32) .. +7
+template <int RL = BG_N>
 MOE_DEV bf16x8 tr_frag(const bf16_t* st, int kbase, int i0, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int col = i0 + 16 * (g & 1) + 4 * (s & 3);
@@ -61,7 +62,7 @@ MOE_DEV bf16x8 tr_frag(const bf16_t* st, int kbase, int i0, int lane) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int k = kbase + 8 * (g >> 1) + 4 * q + (s >> 2);
-    const bf16_t* p = st + k * BG_N + (kswz(k, col >> 3) << 3) + (col & 7);
+    const bf16_t* p = st + k * RL + (kswz(k, col >> 3) << 3) + (col & 7);
     h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_v4i16*)((__attribute__((address_space(3))) bf16_t*)p));
   }
@@ -217,18 +218,28 @@ __global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
 // out[e][m][n] = sum over expert e's rows r of A[r][m] B[r][n], float32.
 // MODE 0: dW_down (A = dY [.][hidden], B = H [.][inter]);
 // MODE 1: dW_gate (A = dG [.][inter], B = X [.][hidden]); MODE 2: dW_up (A = dU).
+// Tile 128 (m) x 256 (n); wave tile 64 x 128 (2 x 4 MFMA blocks).  Both
+// operands are staged as k-rows (one per token row, 32 per step): A rows of
+// 128, B rows of 256 elements.  Rows past the expert's count read beyond the
+// buffer, which returns zeros, so they add nothing.
+namespace {
+constexpr int WG_N = 256;                               // n columns per tile
+constexpr int WG_STAGE = BG_K * BG_M + BG_K * WG_N;     // bf16 elements per stage (A then B)
+constexpr int WG_ACP = BG_K * BG_M * 2 / 1024 / BG_NWAVE;  // 1 KB A copies per wave per step (2)
+constexpr int WG_BCP = BG_K * WG_N * 2 / 1024 / BG_NWAVE;  // ... B copies (4)
+}  // namespace
+
 template <int MODE>
 __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[BG_NS * 2 * BG_K * BG_N];
-  constexpr int STG = 2 * BG_K * BG_N;           // A k-rows then B k-rows
+  __shared__ __attribute__((aligned(16))) bf16_t smem[BG_NS * WG_STAGE];
   const int M = MODE == 0 ? g.H : g.I;
   const int N = MODE == 0 ? g.I : g.H;
-  const int tm = M / BG_M, tn = N / BG_N;
+  const int tm = M / BG_M, tn = N / WG_N;
   const int e = blockIdx.x / (tm * tn);
   if (e >= g.n_exp) return;  // uniform
   const int t = blockIdx.x - e * tm * tn;
   const int mt = t / tn, ntile = t - mt * tn;
-  const int m0 = mt * BG_M, n0 = ntile * BG_N;
+  const int m0 = mt * BG_M, n0 = ntile * WG_N;
   int row_base, cnt;
   expert_rows(g, e, row_base, cnt);
   const int nk = (cnt + BG_K - 1) / BG_K;
@@ -242,37 +253,42 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
   const bf16_t* bp = MODE == 0 ? g.hst : g.xst;
   const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(ap, total_rows * uint32_t(M) * 2u);
   const __amdgpu_buffer_rsrc_t br = buffer_rsrc(bp, total_rows * uint32_t(N) * 2u);
-  // copy i of wave w covers k-rows 4 (2w+i) .. +3 of the step (lane l: + l/16,
-  // position l%16); k-rows past the expert's rows read beyond the buffer, which
-  // returns zeros
-  uint32_t acol[2], bcol[2];
-  int krow[2];
+  // A copy i of wave w: k-rows 4 (2w+i) .. +3 (lane l: + l/16, position l%16);
+  // B copy i: k-rows 2 (4w+i) .. +1 (lane l: + l/32, position l%32)
+  uint32_t acol[WG_ACP], bcol[WG_BCP];
+  int akr[WG_ACP], bkr[WG_BCP];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    krow[i] = 4 * (2 * wave + i) + (lane >> 4);
-    acol[i] = uint32_t(m0 + kswz(krow[i], lane & 15) * 8);
-    bcol[i] = uint32_t(n0 + kswz(krow[i], lane & 15) * 8);
+  for (int i = 0; i < WG_ACP; ++i) {
+    akr[i] = 4 * (WG_ACP * wave + i) + (lane >> 4);
+    acol[i] = uint32_t(m0 + kswz(akr[i], lane & 15) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < WG_BCP; ++i) {
+    bkr[i] = 2 * (WG_BCP * wave + i) + (lane >> 5);
+    bcol[i] = uint32_t(n0 + kswz(bkr[i], lane & 31) * 8);
   }
   auto copy_step = [&](int kt) {
     const int k = min(kt, max(nk - 1, 0));
-    bf16_t* st = smem + (kt % BG_NS) * STG;
+    bf16_t* st = smem + (kt % BG_NS) * WG_STAGE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = k * BG_K + krow[i];
-      const bool ok = r < cnt;
-      const uint32_t row = uint32_t(row_base + r);
-      const uint32_t ao = ok ? (row * uint32_t(M) + acol[i]) * 2u : 0xfffffff0u;
-      const uint32_t bo = ok ? (row * uint32_t(N) + bcol[i]) * 2u : 0xfffffff0u;
-      copy16_to_lds(ar, ao, st + 4 * (2 * wave + i) * BG_N);
-      copy16_to_lds(br, bo, st + BG_K * BG_N + 4 * (2 * wave + i) * BG_N);
+    for (int i = 0; i < WG_ACP; ++i) {
+      const int r = k * BG_K + akr[i];
+      const uint32_t o = r < cnt ? (uint32_t(row_base + r) * uint32_t(M) + acol[i]) * 2u : 0xfffffff0u;
+      copy16_to_lds(ar, o, st + 4 * (WG_ACP * wave + i) * BG_M);
+    }
+#pragma unroll
+    for (int i = 0; i < WG_BCP; ++i) {
+      const int r = k * BG_K + bkr[i];
+      const uint32_t o = r < cnt ? (uint32_t(row_base + r) * uint32_t(N) + bcol[i]) * 2u : 0xfffffff0u;
+      copy16_to_lds(br, o, st + BG_K * BG_M + 2 * (WG_BCP * wave + i) * WG_N);
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -280,21 +296,22 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
     copy_step(0);
     copy_step(1);
     for (int kt = 0; kt < nk; ++kt) {
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(BG_CPW));
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(WG_ACP + WG_BCP));  // this wave's copies of kt landed
       __builtin_amdgcn_s_barrier();
       copy_step(kt + 2);
-      const bf16_t* st = smem + (kt % BG_NS) * STG;
+      const bf16_t* st = smem + (kt % BG_NS) * WG_STAGE;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        bf16x8 af[2], bf[2];
+        bf16x8 af[2], bf[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = tr_frag(st, 16 * s, wm * 64 + 32 * i, lane);
+        for (int i = 0; i < 2; ++i) af[i] = tr_frag<BG_M>(st, 16 * s, wm * 64 + 32 * i, lane);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = tr_frag(st + BG_K * BG_N, 16 * s, wn * 64 + 32 * j, lane);
+        for (int j = 0; j < 4; ++j)
+          bf[j] = tr_frag<WG_N>(st + BG_K * BG_M, 16 * s, wn * 128 + 32 * j, lane);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
       }
     }
@@ -305,8 +322,8 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + 32 * j + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -564,7 +581,7 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
                          dim3(BG_NT), 0, st, g);
       break;
     case 6: {  // weight gradients
-      const unsigned tiles = unsigned((H / BG_M) * (I / BG_N) * (E + S));
+      const unsigned tiles = unsigned((H / BG_M) * (I / WG_N) * (E + S));
       hipLaunchKernelGGL(wgrad_gemm_kernel<0>, dim3(tiles), dim3(BG_NT), 0, st, g);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       hipLaunchKernelGGL(wgrad_gemm_kernel<1>, dim3(tiles), dim3(BG_NT), 0, st, g);

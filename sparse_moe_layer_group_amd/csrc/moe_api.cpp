@@ -405,6 +405,7 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
 // buffer must span less than 4 GiB.
 int validate_bwd(const moe_cfg* c, int64_t T) {
   if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (c->hidden % 256 != 0 || c->inter % 256 != 0) return MOE_ERR_SHAPE;  // wgrad tiles of 256
   const int64_t rows = T * int64_t(c->topk + c->n_shared);
   if (rows * std::max<int64_t>(c->hidden, c->inter) * 2 >= (int64_t(1) << 32) - 256) return MOE_ERR_SHAPE;
   if (int64_t(c->hidden) * c->inter * 2 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
