@@ -40,10 +40,10 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> gemm_gate_up counters per launch
-    "decode": {"src_sha256": "c875e62590295a1f87d56ac298a1e004947bd7d8f21c5abc0788659ce6399ed5",
-               "fetch_kib": 8153779.9, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "b2a33c33e215b2456d61a803fa6107fe51b8ff34dad7e115e445688407780812",
-                "fetch_kib": 12314692.0, "write_kib": 294912.2},
+    "decode": {"src_sha256": "f2b5447817cca990eadef93fc9e9451701b7155f534b28d3d3712356d48af261",
+               "fetch_kib": 8153701.1, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "ebb28573addc9f755a5e58341d54c853f8c77c88e60ed23180e0a7b9011d83ec",
+                "fetch_kib": 12321364.2, "write_kib": 294912.1},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
