@@ -240,8 +240,9 @@ int moe_quantize_1x128(const void* x, int64_t rows, int32_t cols, uint8_t* q, fl
 
 /*
  * Kernel timing instrumentation (off by default; not thread-safe).
- * While enabled, every kernel launch of moe_route / moe_forward /
- * moe_bias_update is bracketed by a pair of HIP events on the caller's stream.
+ * While enabled, every kernel launch (or, in moe_backward, every stage of
+ * launches) of the compute entry points is bracketed by a pair of HIP events
+ * on the caller's stream.
  * moe_profile_read waits for the recorded events, adds each pair's elapsed
  * time to the slot of its kernel, clears the record, and returns the number
  * of slots (at most n_slots are written to total_ms / launches, which may be

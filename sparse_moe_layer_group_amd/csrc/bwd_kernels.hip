@@ -11,9 +11,10 @@
 // rows offsets[e] .. offsets[e] + counts[e] - 1 in expert order (perm gives
 // their token ids), then the shared expert's T rows (row T*K + t is token t).
 //
-// GEMMs.  Two LDS-tiled grouped GEMMs on 32x32x16 bf16 MFMAs (128 x 128 tiles,
-// K steps of 32, four waves of 64 x 64, three LDS stages filled two steps ahead
-// by buffer_load ... lds copies):
+// GEMMs.  Two LDS-tiled grouped GEMMs on 32x32x16 bf16 MFMAs (K steps of 32,
+// four waves, three LDS stages filled two steps ahead by buffer_load ... lds
+// copies; dgrad tiles 128 x 128 with waves of 64 x 64, wgrad tiles 128 x 256
+// with waves of 64 x 128):
 //   - dgrad:  out[row][n] = sum_k A[row][k] B[k][n] over an expert's rows,
 //     A = staged rows (k contiguous), B = the expert's weight matrix read along
 //     its slow dimension (dH = dY W_down; dX = dG W_gate + dU W_up);
