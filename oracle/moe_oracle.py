@@ -44,6 +44,12 @@ Parity status of each function (what pins it in tests/test_oracle_*.py):
                         layer_fixed_routing in every input; torch CPU autograd
                         of the fixed-routing layer; zero router gradient with
                         one routed expert; linearity in dy)
+  quantize_128x1        pinned (equals quantize_1x128 of the transpose)
+  backward(fp8_emulation) and expert_*_fp8  pinned (with the quantisers
+                        replaced by the identity it equals the pinned backward;
+                        token isolation of dx; exact column equivariance of
+                        dW_down in dy; weight gradients unchanged by a
+                        sub-step change of one dy element)
 """
 from __future__ import annotations
 
@@ -396,6 +402,59 @@ def expert_backward(X: np.ndarray, dY: np.ndarray, wg: np.ndarray, wu: np.ndarra
     return dX, dG.T @ X, dU.T @ X, dwd
 
 
+def expert_swiglu_input_fp8(X: np.ndarray, wg: np.ndarray, wu: np.ndarray):
+    """The E4M3 path's SwiGLU input of one expert, as the backward keeps it.
+
+    [V3] §2.2: the expert inputs are quantised in 1x128 tiles; the SwiGLU
+    input is cached in E4M3 and the SwiGLU output is recomputed from that cache
+    in the backward.  Reading: G = Q(X) W_gate^T and U = Q(X) W_up^T (exact
+    products of the dequantised operands), each cached as Q(G), Q(U) with the
+    1x128 rule along the intermediate dimension.  ``wg``, ``wu`` are the
+    dequantised weights.  Returns (Q(X), Q(G), Q(U)) dequantised, float64.
+    """
+    Xq = fake_quant_1x128(X)
+    return Xq, fake_quant_1x128(Xq @ wg.T), fake_quant_1x128(Xq @ wu.T)
+
+
+def expert_output_fp8(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """One expert's output recomputed on the E4M3 path from the cached SwiGLU
+    input: Y = Q(SiLU(Q(G)) * Q(U)) W_down^T, the SwiGLU output quantised 1x128
+    as the down projection's input ([V3] §2.2)."""
+    _, Gc, Uc = expert_swiglu_input_fp8(X, wg, wu)
+    return fake_quant_1x128(silu(Gc) * Uc) @ wd.T
+
+
+def expert_backward_fp8(X: np.ndarray, dY: np.ndarray, wg: np.ndarray, wu: np.ndarray,
+                        wd: np.ndarray):
+    """Backward of one SwiGLU expert on the E4M3 path ([V3] §2.2), float64.
+
+    The steps of ``expert_backward`` with every GEMM operand in E4M3:
+      - the cached SwiGLU input Q(G), Q(U) (``expert_swiglu_input_fp8``) and
+        the recomputed H = SiLU(Q(G)) * Q(U);
+      - dgrad products contract over the hidden or intermediate dimension, so
+        their activation operands take 1x128 tiles: dH = Q(dY) W_down,
+        dX = Q(dG) W_gate + Q(dU) W_up, with dG = dH * Q(U) * SiLU'(Q(G)) and
+        dU = dH * SiLU(Q(G));
+      - wgrad products contract over the expert's rows (tokens), so both
+        operands take 128x1 tiles, 128 consecutive rows of one column:
+        dW_down = Q'(dY)^T Q'(H), dW_gate = Q'(dG)^T Q'(X), dW_up = Q'(dU)^T Q'(X)
+        (Q' = ``fake_quant_128x1`` over the rows in the order given).
+    The weights ``wg``, ``wu``, ``wd`` are the dequantised 128x128-block E4M3
+    weights; X is the expert's input rows, dY its output gradient rows.
+    Returns (dX, dW_gate, dW_up, dW_down).
+    """
+    _, Gc, Uc = expert_swiglu_input_fp8(X, wg, wu)
+    A = silu(Gc)
+    Hh = A * Uc
+    dH = fake_quant_1x128(dY) @ wd
+    dU = dH * A
+    dG = dH * Uc * dsilu(Gc)
+    dX = fake_quant_1x128(dG) @ wg + fake_quant_1x128(dU) @ wu
+    dwd = fake_quant_128x1(dY).T @ fake_quant_128x1(Hh)
+    Xr = fake_quant_128x1(X)
+    return dX, fake_quant_128x1(dG).T @ Xr, fake_quant_128x1(dU).T @ Xr, dwd
+
+
 def gate_backward(ssel: np.ndarray, dg: np.ndarray) -> np.ndarray:
     """Gradient of the router logits of the chosen experts from the gate gradients.
 
@@ -426,7 +485,8 @@ def backward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: Expert
              dy64: np.ndarray, *, n_groups: int, topk_groups: int, topk: int, group_topn: int = 2,
              n_shared: int = 1, tokens: Optional[Sequence[int]] = None,
              grad_experts: Optional[Sequence[int]] = None,
-             router_cols: Optional[Sequence[int]] = None) -> BackwardResult:
+             router_cols: Optional[Sequence[int]] = None,
+             fp8_emulation: bool = False) -> BackwardResult:
     """Gradients of <dy, y> w.r.t. x, W_r and every expert's three matrices.
 
     Steps, in the order of the forward they reverse ([V3] §1.3 Eq 12-15):
@@ -445,7 +505,16 @@ def backward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: Expert
     (experts whose weight gradients are formed; shared = E), ``router_cols``
     (columns of dW_r).  Gate and logit gradients are formed for the tokens
     these need.  Defaults: everything.
+
+    ``fp8_emulation``: the E4M3 path of [V3] §2.2 (weights given as E4M3 codes
+    and 128x128 block scales): expert outputs from ``expert_output_fp8`` and
+    expert gradients from ``expert_backward_fp8``; an expert's rows are its
+    tokens in ascending order (shared: all tokens), the row order of its
+    128x1 tiles.  Without it, the weights are dequantised and the activations
+    stay exact.
     """
+    ffn_out = expert_output_fp8 if fp8_emulation else expert_ffn
+    ffn_bwd = expert_backward_fp8 if fp8_emulation else expert_backward
     T, H = x64.shape
     E = wr64.shape[1]
     L, s32, r, p = route(x64, wr64, b32, n_groups=n_groups, topk_groups=topk_groups, topk=topk,
@@ -473,7 +542,7 @@ def backward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: Expert
         for e in sorted(set(int(v) for v in sel.reshape(-1))):
             jj, kk = np.nonzero(sel == e)
             wg, wu, wd = expert_f64(experts(e))
-            Y = expert_ffn(x64[need[jj]], wg, wu, wd)
+            Y = ffn_out(x64[need[jj]], wg, wu, wd)
             dg[need[jj], kk] = np.einsum("rh,rh->r", dy64[need[jj]], Y)
     # step 3
     dL = np.zeros((T, topk), dtype=F64)
@@ -510,7 +579,7 @@ def backward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: Expert
             if e in gexp:
                 dw[e] = (np.zeros_like(wg), np.zeros_like(wu), np.zeros_like(wd))
             continue
-        dX, dwg, dwu, dwd = expert_backward(x64[rows], dY, wg, wu, wd)
+        dX, dwg, dwu, dwd = ffn_bwd(x64[rows], dY, wg, wu, wd)
         if e in gexp:
             dw[e] = (dwg, dwu, dwd)
         for i, t in enumerate(rows):
@@ -671,6 +740,38 @@ def fake_quant_1x128(a: np.ndarray) -> np.ndarray:
     """Quantise then dequantise (float64 result): the emulation mode's activation map."""
     q, s = quantize_1x128(np.asarray(a, dtype=F64).astype(F32))
     return dequantize_1x128(q, s)
+
+
+def quantize_128x1(a: np.ndarray):
+    """Per-column, per-128-row quantisation: the 128x1 tiles of [V3] §2.2.
+
+    A product that contracts over tokens (a weight gradient) needs its scales
+    to run along the tokens, so each tile is 128 consecutive rows of one
+    column.  Same rule as ``quantize_1x128``: scale = amax / 448 in float32 (1
+    for an all-zero tile), code = RNE(v / scale) in float32.  Rows are grouped
+    from the first; a last partial group holds the remaining rows (zero
+    padding would change neither its amax nor any product).
+
+    Returns (codes uint8 [R][C], scales float32 [ceil(R/128)][C]).
+    """
+    a32 = np.asarray(a, dtype=F32)
+    R, C = a32.shape
+    codes = np.zeros((R, C), dtype=np.uint8)
+    scales = np.ones((-(-R // 128), C), dtype=F32)
+    for blk in range(scales.shape[0]):
+        t = a32[128 * blk:128 * (blk + 1)]
+        amax = np.abs(t).max(axis=0)
+        sc = np.where(amax > 0, (amax / F32(448.0)).astype(F32), F32(1.0)).astype(F32)
+        scales[blk] = sc
+        codes[128 * blk:128 * (blk + 1)] = e4m3_quantize((t / sc[None, :]).astype(F32))
+    return codes, scales
+
+
+def fake_quant_128x1(a: np.ndarray) -> np.ndarray:
+    """``quantize_128x1`` then dequantise (float64 result)."""
+    q, sc = quantize_128x1(np.asarray(a, dtype=F64).astype(F32))
+    rows = np.repeat(sc.astype(F64), 128, axis=0)[:q.shape[0]]
+    return e4m3_decode(q) * rows
 
 
 # ----------------------------------------------------------------------------

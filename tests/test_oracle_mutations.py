@@ -9,6 +9,7 @@ import pytest
 import oracle
 import oracle.moe_oracle as M
 from tests import test_oracle_backward as TBW
+from tests import test_oracle_backward_fp8 as TB8
 from tests import test_oracle_balance as TB
 from tests import test_oracle_ffn as TF
 from tests import test_oracle_fp8 as T8
@@ -24,7 +25,7 @@ _orig = {n: getattr(M, n) for n in ("group_scores", "biased_scores", "gate_value
                                      "expert_ffn", "bias_update", "router_affinity",
                                      "e4m3_quantize", "select_experts",
                                      "sequence_balance_loss", "dsilu", "gate_backward",
-                                     "expert_backward")}
+                                     "expert_backward", "expert_swiglu_input_fp8")}
 
 
 def m_group_top1(z, n_groups, group_topn):
@@ -115,6 +116,45 @@ def m_expert_bwd_swapped(X, dY, wg, wu, wd):
     return dX, dwu, dwg, dwd
 
 
+def m_fp8_wgrad_dy_1x128(X, dY, wg, wu, wd):
+    # dW_down from 1x128 tiles of dY (the dgrad grouping) instead of 128x1
+    _, Gc, Uc = _orig["expert_swiglu_input_fp8"](X, wg, wu)
+    A = M.silu(Gc)
+    dH = M.fake_quant_1x128(dY) @ wd
+    dU, dG = dH * A, dH * Uc * M.dsilu(Gc)
+    dX = M.fake_quant_1x128(dG) @ wg + M.fake_quant_1x128(dU) @ wu
+    Xr = M.fake_quant_128x1(X)
+    return (dX, M.fake_quant_128x1(dG).T @ Xr, M.fake_quant_128x1(dU).T @ Xr,
+            M.fake_quant_1x128(dY).T @ M.fake_quant_128x1(A * Uc))
+
+
+def m_fp8_dgrad_dy_exact(X, dY, wg, wu, wd):
+    # dH from the unquantised dY
+    _, Gc, Uc = _orig["expert_swiglu_input_fp8"](X, wg, wu)
+    A = M.silu(Gc)
+    dH = dY @ wd
+    dU, dG = dH * A, dH * Uc * M.dsilu(Gc)
+    dX = M.fake_quant_1x128(dG) @ wg + M.fake_quant_1x128(dU) @ wu
+    Xr = M.fake_quant_128x1(X)
+    return (dX, M.fake_quant_128x1(dG).T @ Xr, M.fake_quant_128x1(dU).T @ Xr,
+            M.fake_quant_128x1(dY).T @ M.fake_quant_128x1(A * Uc))
+
+
+def m_q128x1_per_row(a):
+    # amax taken along each row of a tile instead of down each column
+    a32 = np.asarray(a, dtype=np.float32)
+    R, C = a32.shape
+    codes = np.zeros((R, C), dtype=np.uint8)
+    scales = np.ones((-(-R // 128), C), dtype=np.float32)
+    for blk in range(scales.shape[0]):
+        t = a32[128 * blk:128 * (blk + 1)]
+        amax = np.abs(t).max(axis=1, keepdims=True)
+        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        scales[blk] = sc.max()
+        codes[128 * blk:128 * (blk + 1)] = M.e4m3_quantize((t / sc).astype(np.float32))
+    return codes, scales
+
+
 CASES = [
     ("group_scores", m_group_top1, TR.test_selection_matches_subset_enumeration, (0,)),
     ("biased_scores", m_no_bias, TR.test_large_bias_forces_and_excludes_experts, ()),
@@ -134,6 +174,11 @@ CASES = [
     ("gate_backward", m_gate_bwd_uncentred, TBW.test_directional_derivatives_match_finite_differences,
      ("w_router",)),
     ("expert_backward", m_expert_bwd_swapped, TBW.test_gradients_match_torch_autograd, ()),
+    ("expert_backward_fp8", m_fp8_wgrad_dy_1x128,
+     TB8.test_doubling_a_dy_column_doubles_that_row_of_dw_down, ()),
+    ("expert_backward_fp8", m_fp8_dgrad_dy_exact,
+     TB8.test_a_substep_change_of_dy_moves_no_weight_gradient, ()),
+    ("quantize_128x1", m_q128x1_per_row, TB8.test_quantize_128x1_is_1x128_of_the_transpose, ()),
 ]
 
 
