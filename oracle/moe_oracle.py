@@ -672,19 +672,27 @@ def sequence_balance_loss(s32: np.ndarray, topk: int, seq_len: int, alpha: float
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
     """Value of each OCP E4M3FN code (1 sign, 4 exponent bits biased by 7, 3 mantissa bits).
 
     Exponent field 0 holds subnormals m * 2^-9; field 15 with mantissa 7 is NaN
     (the format has no infinities).
     """
-    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    c = np.asarray(c, dtype=np.int64) & 0xFF
     sign = np.where(c & 0x80, -1.0, 1.0)
     ef = (c >> 3) & 0xF
     m = (c & 0x7).astype(F64)
     val = np.where(ef == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(ef.astype(F64) - 7.0))
     val = np.where((ef == 15) & ((c & 7) == 7), np.nan, val)
     return sign * val
+
+
+_E4M3_VALUES = _e4m3_value(np.arange(256))   # the 256 codes' values, looked up by code
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each E4M3FN code (``_e4m3_value``), float64."""
+    return _E4M3_VALUES[np.asarray(codes).astype(np.uint8)]
 
 
 def e4m3_quantize(v) -> np.ndarray:
@@ -712,21 +720,28 @@ def e4m3_quantize(v) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def _tile_scale(amax: np.ndarray) -> np.ndarray:
+    """amax / 448 in float32; 1 where that is zero (an all-zero tile, or a
+    max-abs so small that the quotient underflows)."""
+    sc = (np.asarray(amax, dtype=F32) / F32(448.0)).astype(F32)
+    return np.where(sc > 0, sc, F32(1.0)).astype(F32)
+
+
 def quantize_1x128(a: np.ndarray):
     """Per-row, per-128-column online quantisation of an activation matrix.
 
     [V3] §2.2: activations are grouped in 1x128 tiles (one token, 128
     channels); each tile's scale comes from its current max-abs value and the
     values are stored as E4M3.  Reading: scale = amax / 448 in float32 (1 for an
-    all-zero tile); code = RNE(v / scale) computed in float32.
+    all-zero tile, and wherever amax / 448 rounds to zero); code = RNE(v / scale)
+    computed in float32.
 
     Returns (codes uint8 [R][C], scales float32 [R][C/128]).
     """
     a32 = np.asarray(a, dtype=F32)
     R, C = a32.shape
     t = a32.reshape(R, C // 128, 128)
-    amax = np.abs(t).max(axis=2)
-    scale = np.where(amax > 0, (amax / F32(448.0)).astype(F32), F32(1.0)).astype(F32)
+    scale = _tile_scale(np.abs(t).max(axis=2))
     ratio = (t / scale[:, :, None]).astype(F32)
     return e4m3_quantize(ratio).reshape(R, C), scale
 
@@ -748,7 +763,7 @@ def quantize_128x1(a: np.ndarray):
     A product that contracts over tokens (a weight gradient) needs its scales
     to run along the tokens, so each tile is 128 consecutive rows of one
     column.  Same rule as ``quantize_1x128``: scale = amax / 448 in float32 (1
-    for an all-zero tile), code = RNE(v / scale) in float32.  Rows are grouped
+    where that is zero), code = RNE(v / scale) in float32.  Rows are grouped
     from the first; a last partial group holds the remaining rows (zero
     padding would change neither its amax nor any product).
 
@@ -760,8 +775,7 @@ def quantize_128x1(a: np.ndarray):
     scales = np.ones((-(-R // 128), C), dtype=F32)
     for blk in range(scales.shape[0]):
         t = a32[128 * blk:128 * (blk + 1)]
-        amax = np.abs(t).max(axis=0)
-        sc = np.where(amax > 0, (amax / F32(448.0)).astype(F32), F32(1.0)).astype(F32)
+        sc = _tile_scale(np.abs(t).max(axis=0))
         scales[blk] = sc
         codes[128 * blk:128 * (blk + 1)] = e4m3_quantize((t / sc[None, :]).astype(F32))
     return codes, scales
