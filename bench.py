@@ -133,6 +133,9 @@ def main():
                     choices=["decode", "prefill", "skew", "fp8", "backward"])
     ap.add_argument("--backward-shape", default="prefill", choices=["decode", "prefill"],
                     help="backward workload: batch shape (prefill T=8192 or decode T=256)")
+    ap.add_argument("--backward-weights", default="bf16", choices=["bf16", "e4m3"],
+                    help="backward workload: expert weights in bf16, or E4M3 with 128x128 block "
+                         "scales (every expert GEMM in E4M3; inputs of the fp8 workload)")
     ap.add_argument("--skew-steps", type=int, default=200,
                     help="skew workload: bias-update steps (forward timed at first, middle, last)")
     ap.add_argument("--cpu-tokens", type=int, default=32,
@@ -321,11 +324,16 @@ def bench_backward(args, np, torch, moe, S):
     tokens/s of the backward, and the roofline of its dominant kernel, the
     weight-gradient GEMMs (float32 gradients of all 257 experts' matrices)."""
     dev = torch.device("cuda:0")
-    c = S.get_config(args.backward_shape)
+    shape = S.get_config(args.backward_shape)
+    f8 = args.backward_weights == "e4m3"
+    # E4M3: the fp8 workload's inputs (outliers included) at the shape's batch size
+    c = S.get_config("fp8", T=shape.T) if f8 else shape
     cfg = moe.cfg_from(c)
     T, H, I, E, K, Sn = c.T, c.hidden, c.inter, c.n_experts, c.topk, c.n_shared
     n = E + Sn
-    log(f"backward on the {c.name} batch: T={T}; generating inputs on the GPU")
+    wb = 1 if f8 else 2   # bytes per weight element
+    log(f"backward on the {shape.name} batch, {c.w_dtype} weights: T={T}; generating inputs on "
+        f"the GPU")
     x = S.gen_x(c, device=dev)
     wr = S.gen_router(c, device=dev)
     b = S.gen_bias(c, device=dev)
@@ -364,26 +372,29 @@ def bench_backward(args, np, torch, moe, S):
             log(f"  {k:18s} {kms / nn * 1e3:9.1f} us/call  ({nn} calls)")
 
     rows = T * K + Sn * T
+    mfma_peak = MFMA_PEAK_TFLOPS["e4m3" if f8 else "bf16"]
     # weight-gradient GEMMs (one call = three launches: dW_down, dW_gate, dW_up):
     # float32 gradients of every expert written once, staged operands read once
-    # per launch (dY and H; dG and X; dU and X)
+    # per launch (dY and H; dG and X; dU and X), wb bytes per element (E4M3:
+    # their 128x1 codes)
     wg_ms, wg_n = kern["bwd_wgrad"]
     wg_s = wg_ms / max(wg_n, 1) / 1e3
-    wg_bytes = n * 3 * H * I * 4 + rows * (3 * H + 3 * I) * 2
+    wg_bytes = n * 3 * H * I * 4 + rows * (3 * H + 3 * I) * wb
     wg_flops = 3 * 2 * rows * H * I
     roofline = {"bound": "hbm", "achieved": round(wg_bytes / wg_s / 1e9, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(wg_bytes / wg_s / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": None, "kernel": "bwd_wgrad (dW_down, dW_gate, dW_up launches)",
                 "kernel_us": round(wg_s * 1e6, 2), "alg_bytes_per_launch": int(wg_bytes),
                 "alg_flops_per_launch": int(wg_flops),
-                "mfma_frac": round(wg_flops / wg_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+                "mfma_frac": round(wg_flops / wg_s / 1e12 / mfma_peak, 4)}
     # the whole backward: expert recompute, dgrad and wgrad (3 x the forward's
     # expert flops) plus the router's; weights read twice, gradients written
     bw_flops = 3 * rows * 2 * 3 * H * I + 2 * T * K * H * 2
-    bw_bytes = 2 * n * 3 * H * I * 2 + n * 3 * H * I * 4 + 3 * T * H * 2 + 2 * H * E * 4
+    bw_bytes = 2 * n * 3 * H * I * wb + n * 3 * H * I * 4 + 3 * T * H * 2 + 2 * H * E * 4
     backward = {"ms": round(ms, 4), "alg_bytes": int(bw_bytes), "alg_flops": int(bw_flops),
                 "hbm_frac": round(bw_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                "mfma_frac": round(bw_flops / (ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                "mfma_frac": round(bw_flops / (ms / 1e3) / 1e12 / mfma_peak, 4),
+                "weights": c.w_dtype,
                 "kernels_us": {k: round(v / nn * 1e3, 1) for k, (v, nn) in kern.items() if nn}}
     cpu = None
     if args.cpu_tokens > 0:
@@ -392,11 +403,12 @@ def bench_backward(args, np, torch, moe, S):
         "metric": "MoE-layer backward tokens/s on 1 MI355X (one training step's layer gradients)",
         "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": c.w_dtype,
         "data": "synthetic (seeded SplitMix64 inputs and upstream gradient, V3 layer shapes)",
-        "config": {"workload": f"backward on the {c.name} batch: DeepSeek-V3 MoE layer gradients "
-                               f"(dx, dW_r, dW of 257 experts in float32), T={T}, hidden {H}, "
-                               f"inter {I}, {E} routed + {Sn} shared, top-{K}, bf16",
+        "config": {"workload": f"backward on the {shape.name} batch: DeepSeek-V3 MoE layer "
+                               f"gradients (dx, dW_r, dW of 257 experts in float32), T={T}, hidden "
+                               f"{H}, inter {I}, {E} routed + {Sn} shared, top-{K}, "
+                               + ("E4M3 weights and GEMM operands" if f8 else "bf16"),
                    "T": T, "hidden": H, "inter": I, "n_experts": E, "n_shared": Sn, "topk": K},
         "roofline": roofline, "backward": backward, "cpu_baseline": cpu,
     }
@@ -420,13 +432,16 @@ def cpu_baseline_backward(c, n_tok, x_dev, b_dev, dy_cpu):
     cache = {e: S.gen_expert(c, e, "cpu") for e in touched}
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
+    f8 = c.w_dtype == "e4m3"
     O.backward(x, wr, b, lambda e: cache[e], dy, n_groups=c.n_groups, topk_groups=c.topk_groups,
-               topk=c.topk, group_topn=c.group_topn, n_shared=c.n_shared, grad_experts=touched)
+               topk=c.topk, group_topn=c.group_topn, n_shared=c.n_shared, grad_experts=touched,
+               fp8_emulation=f8)
     dt = time.perf_counter() - t0
     log(f"cpu baseline: oracle backward of {n_tok} tokens ({len(touched)} experts' gradients) "
         f"in {dt:.1f}s on {cores} cores")
     return {"value": round(n_tok / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle backward of the first {n_tok} tokens as their own batch "
+            "sample": f"float64 oracle backward{' (E4M3 emulation)' if f8 else ''} of the first "
+                      f"{n_tok} tokens as their own batch "
                       f"(dx, dW_r, and dW of the {len(touched)} experts they touch, shared included)"}
 
 

@@ -203,15 +203,25 @@ int moe_balance_loss(const moe_cfg* cfg, int64_t T, int32_t seq_len, const void*
  * none.  Gates are the normalised raw affinities of the chosen experts
  * (Eq 13); their gradient flows through the normalisation and the sigmoid
  * into x and W_r.
- *   x, w_router, bias, w   as in moe_forward (BF16 activations and weights
- *                          only; other dtypes return MOE_ERR_DTYPE; hidden
- *                          and inter multiples of 256, else MOE_ERR_SHAPE)
+ *   x, w_router, bias, w   as in moe_forward (BF16 activations with BF16 or
+ *                          E4M3 weights; other dtypes return MOE_ERR_DTYPE;
+ *                          hidden and inter multiples of 256, else
+ *                          MOE_ERR_SHAPE)
  *   dy        device bf16 [T][H] upstream gradient
  *   dx        device bf16 [T][H] out
  *   dw_router device float [H][E] out
  *   dw_gate, dw_up  device float [E+S][I][H] out (experts without tokens: 0)
  *   dw_down   device float [E+S][H][I] out
  *   ws        workspace of at least moe_backward_workspace_bytes(cfg, T) bytes
+ * E4M3 weights (§2.2): every expert GEMM takes E4M3 operands.  The SwiGLU
+ * input G, U is recomputed from x quantised in 1x128 tiles and kept as
+ * 1x128 E4M3; H is recomputed from it.  The output gradients g dy and the
+ * gradients dG, dU are quantised in 1x128 tiles for the data-gradient GEMMs;
+ * the weight-gradient GEMMs, which contract over an expert's rows, take both
+ * operands in 128x1 tiles (per column, 128 consecutive rows of the expert
+ * from its first row).  Scales follow moe_quantize_1x128's rule.  The
+ * weights are transposed into the workspace on every call (three E4M3 copies
+ * of the weights, about 3 * (E+S) * H * I bytes).
  * Every output is overwritten.  Sums over tokens and experts run in a fixed
  * order (deterministic).  Staged rows use 32-bit offsets: T * (K + S) *
  * max(H, I) * 2 must stay below 4 GiB, and H * I * 2 too (else MOE_ERR_SHAPE).
@@ -230,7 +240,7 @@ int moe_backward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_ro
  *   x      device bfloat16 [rows][cols], cols % 128 == 0 (else MOE_ERR_SHAPE)
  *   q      device uint8 [rows][cols]: OCP E4M3FN codes
  *   scales device float [rows][cols/128]
- * Per slice: scale = amax / 448 in float32 (1 when amax == 0); each code is
+ * Per slice: scale = amax / 448 in float32 (1 where that is 0); each code is
  * the float32 quotient v / scale (IEEE division) rounded to nearest, ties to
  * even, saturated at +-448.  rows == 0 returns MOE_OK without reading
  * pointers.

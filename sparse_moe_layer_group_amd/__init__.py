@@ -291,8 +291,12 @@ def backward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Ten
     _check(dw_gate, "dw_gate", torch.float32, (n, I, H))
     _check(dw_up, "dw_up", torch.float32, (n, I, H))
     _check(dw_down, "dw_down", torch.float32, (n, H, I))
-    ex = _Experts(experts["w_gate"].data_ptr(), experts["w_up"].data_ptr(),
-                  experts["w_down"].data_ptr(), None, None, None)
+    if cfg.w_dtype == E4M3:
+        _check(experts.get("s_gate"), "s_gate", torch.float32, (n, I // 128, H // 128))
+        _check(experts.get("s_up"), "s_up", torch.float32, (n, I // 128, H // 128))
+        _check(experts.get("s_down"), "s_down", torch.float32, (n, H // 128, I // 128))
+    ex = _Experts(*[experts[k].data_ptr() if experts.get(k) is not None else None
+                    for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")])
     rc = lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(bias),
                             ctypes.byref(ex), _ptr(dy), _ptr(dx), _ptr(dw_router), _ptr(dw_gate),
                             _ptr(dw_up), _ptr(dw_down), _ptr(ws),

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["moe_api.cpp", "route_kernels.hip", "gemm_kernels.hip", "stream_gemm.hip", "tile_gemm.hip",
-           "fp8_kernels.hip", "balance_kernels.hip", "bwd_kernels.hip"]
+           "fp8_kernels.hip", "balance_kernels.hip", "bwd_kernels.hip", "bwd_fp8_kernels.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code.

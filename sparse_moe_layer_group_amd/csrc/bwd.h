@@ -46,4 +46,92 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
                                    const bf16_t* dy, bf16_t* dx, float* dw_router, hipStream_t st,
                                    int stage);
 
+// ---- E4M3 backward (bwd_fp8_kernels.hip)
+
+// One grouped E4M3 GEMM launch (see f8_gemm_kernel): sources 0 and 1 (the
+// second only for dX), output float32 or bf16.
+struct F8GemmArgs {
+  const uint8_t* a0;
+  const uint8_t* a1;
+  const float* as0;
+  const float* as1;
+  const uint8_t* b0;
+  const uint8_t* b1;
+  const float* bs0;
+  const float* bs1;
+  void* out;
+  const int32_t* perm;     // A rows gathered through perm (row grouping), or null
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* mt;       // [n_exp+1] prefix of 128-row tiles
+  const int32_t* kp;       // [n_exp+1] prefix of rows rounded up to 128
+  int E, n_exp, T, TK, M, N, K;
+};
+
+// Buffers of the E4M3 backward; rows are staged rows.
+struct BwdArgs8 {
+  const bf16_t* x;            // [T][H]
+  const bf16_t* dy;           // [T][H]
+  const int32_t* perm;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* slot;
+  const float* gate;          // [T*K]
+  const uint8_t* xq;          // [T][H] x in E4M3, scales [T][H/128]
+  const float* xs;
+  const uint8_t* w_gate;      // [E+S][I][H] codes, block scales [E+S][I/128][H/128]
+  const uint8_t* w_up;
+  const uint8_t* w_down;      // [E+S][H][I], scales [E+S][H/128][I/128]
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  uint8_t* wgT;               // [E+S][H][I] transposed codes, scales [E+S][H/128][I/128]
+  uint8_t* wuT;
+  uint8_t* wdT;               // [E+S][I][H], scales [E+S][I/128][H/128]
+  float* sgT;
+  float* suT;
+  float* sdT;
+  float* f32a;                // [rows][I] G, then dH
+  float* f32b;                // [rows][I] U
+  uint8_t* gq;                // cached SwiGLU input [rows][I], scales [rows][I/128]
+  float* gs;
+  uint8_t* uq;
+  float* us;
+  uint8_t* hq;                // H for the down GEMM [rows][I], scales [rows][I/128]
+  float* hs;
+  uint8_t* dyq;               // [rows][H], scales [rows][H/128]
+  float* dys;
+  float* rowgate;             // [T*K] gate of each routed staged row
+  float* dg32;                // [rows][I]
+  float* du32;
+  uint8_t* dgq;               // [rows][I], scales [rows][I/128]
+  float* dgs;
+  uint8_t* duq;
+  float* dus;
+  bf16_t* dxst;               // [rows][H]
+  int32_t* mt;                // [E+S+1]
+  int32_t* kp;                // [E+S+1]
+  uint8_t* dyT;               // 128x1 operands: per expert [C][Kp_e], scales [C][Kp_e/128]
+  float* dysT;
+  uint8_t* xT;
+  float* xsT;
+  uint8_t* hT;
+  float* hsT;
+  uint8_t* dgT;
+  float* dgsT;
+  uint8_t* duT;
+  float* dusT;
+  float* dw_gate;
+  float* dw_up;
+  float* dw_down;
+  int E, n_exp, T, TK, K, H, I;
+};
+
+int f8_max_row_tiles(int T, int K, int E, int S);
+
+// One stage of the E4M3 backward: 0 transposed weights, 1 prefixes, 2 G, U
+// and H, 3 Q(dY), 4 dH and the SwiGLU backward, 5 dX, 6 the 128x1 operands,
+// 7 weight gradients.
+hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage);
+
 }  // namespace moe

@@ -359,7 +359,8 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ 
 
 // Per token t: for each chosen expert k, the gate gradient dg = <dy_t, Y_k[t]>
 // (fixed-order block reduction) and the expert's output gradient g_k dy_t; the
-// shared expert's output gradient is dy_t itself.
+// shared expert's output gradient is dy_t itself.  dyst == nullptr: gate
+// gradients only.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dy,
                                                           const bf16_t* __restrict__ yst,
                                                           const int32_t* __restrict__ slot,
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = H / 8;
   const u32x4* d8 = reinterpret_cast<const u32x4*>(dy + size_t(t) * H);
-  if (S > 0) {
+  if (S > 0 && dyst != nullptr) {
     u32x4* o = reinterpret_cast<u32x4*>(dyst + size_t(TK + t) * H);
     for (int c = tid; c < nch; c += 256) o[c] = d8[c];
   }
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
                   (uint32_t(f32_to_bf16(gk * dyf[2 * q + 1])) << 16);
         }
         part[k] += p;
-        reinterpret_cast<u32x4*>(dyst + size_t(sl) * H)[c] = ov;
+        if (dyst != nullptr) reinterpret_cast<u32x4*>(dyst + size_t(sl) * H)[c] = ov;
       }
     }
 #pragma unroll

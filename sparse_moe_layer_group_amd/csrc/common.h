@@ -47,6 +47,35 @@ MOE_DEV float sigmoidf(float v) { return 1.0f / (1.0f + expf(-v)); }
 
 MOE_DEV float siluf(float v) { return v / (1.0f + expf(-v)); }
 
+// ---------------------------------------------------------------- E4M3
+
+// OCP E4M3FN code of a float32 value, round to nearest even, |v| clamped to 448
+MOE_DEV uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  if (a < 0.015625f) {  // below the smallest normal 2^-6: steps of 2^-9
+    return sign | uint32_t(rintf(a * 512.0f));  // 8 lands on the smallest normal's code
+  }
+  uint32_t u = __float_as_uint(a);
+  u += 0x7ffffu + ((u >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
+  return sign | ((u >> 20) - (120u << 3));  // rebias the exponent 127 -> 7
+}
+
+// scale of a quantisation tile from its max-abs value: amax / 448, or 1 where
+// that is zero (an all-zero tile, or a max-abs so small that it underflows)
+MOE_DEV float e4m3_scale(float amax) {
+  const float s = amax / 448.0f;
+  return s > 0.f ? s : 1.0f;
+}
+
+// value of an E4M3FN code (NaN codes are never produced by e4m3_encode)
+MOE_DEV float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? float(m) * 0.001953125f  // subnormal: m * 2^-9
+                           : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
 // ---------------------------------------------------------------- wave helpers
 
 MOE_DEV void argmax_take(float& v, int& i, float ov, int oi) {

@@ -8,7 +8,7 @@
 // full precision and multiplied by the two scales before they join the
 // float32 accumulator.
 //
-// Quantiser: scale = amax / 448 in float32 (1 for an all-zero slice), code =
+// Quantiser: scale = amax / 448 in float32 (1 where that is zero), code =
 // round-to-nearest-even of the float32 quotient v / scale (IEEE division),
 // saturated to +-448.  The encoder is integer arithmetic on the float32 bits,
 // so the codes do not depend on a hardware conversion mode.
@@ -20,22 +20,6 @@
 #include "kernels.h"
 
 namespace moe {
-
-namespace {
-
-// OCP E4M3FN code of a float32 value, round to nearest even, |v| clamped to 448
-MOE_DEV uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.0f);
-  if (a < 0.015625f) {  // below the smallest normal 2^-6: steps of 2^-9
-    return sign | uint32_t(rintf(a * 512.0f));  // 8 lands on the smallest normal's code
-  }
-  uint32_t u = __float_as_uint(a);
-  u += 0x7ffffu + ((u >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
-  return sign | ((u >> 20) - (120u << 3));  // rebias the exponent 127 -> 7
-}
-
-}  // namespace
 
 // ---------------------------------------------------------------- quantiser
 // One 16-lane group per 1x128 slice: lane j holds elements 8j..8j+7.
@@ -62,7 +46,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const bf16_t* __restri
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  const float scale = e4m3_scale(amax);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -385,7 +369,7 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
         float amax = 0.f;
 #pragma unroll
         for (int w = 0; w < FS_NWAVE; ++w) amax = fmaxf(amax, red[w * FS_TBM + r]);
-        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+        const float scale = e4m3_scale(amax);
         if (r < rows) {
           const size_t orow = (size_t)(row_base + m0 + r);
           g.out8[orow * g.N + col] = uint8_t(e4m3_encode(h[i][v] / scale));

@@ -136,12 +136,14 @@ int check_device() {
 enum Slot {
   K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_QUANT, K_BAL,
   K_BWD_RECOMPUTE, K_BWD_COMBINE, K_BWD_DH, K_BWD_DX, K_BWD_WGRAD, K_BWD_ROUTER,
+  K_BWD_WTRANS, K_BWD_RETILE,
   K_NSLOTS
 };
 const char* const kSlotNames[K_NSLOTS] = {
     "router_logits", "select",        "permute",       "gemm_gate_up",  "gemm_down",
     "combine",       "bias_update",   "quantize",      "balance_loss",  "bwd_recompute",
-    "bwd_combine",   "bwd_dgrad_down", "bwd_dgrad_gate_up", "bwd_wgrad", "bwd_router_dx"};
+    "bwd_combine",   "bwd_dgrad_down", "bwd_dgrad_gate_up", "bwd_wgrad", "bwd_router_dx",
+    "bwd_weight_transpose", "bwd_retile_128x1"};
 
 struct Prof {
   bool on = false;
@@ -371,6 +373,9 @@ int run_experts_fp8(const moe_cfg& c, int T, const bf16_t* x, const moe_experts*
 struct BwdLayout {
   Layout f;
   size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dl, dlst, wrt, dwrt, mt, total;
+  // E4M3 weights
+  size_t f32a, f32b, gq, gs, uq, us, dyq, dys, rowgate, dg32, du32, dgq, dgs, duq, dus;
+  size_t wgT, wuT, wdT, sgT, suT, sdT, kp, dyT, dysT, xT, xsT, hT, hsT, dgT, dgsT, duT, dusT;
 };
 
 BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
@@ -384,6 +389,53 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
   };
   const size_t E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
   const size_t TK = size_t(T) * K, rows = TK + S * size_t(T);
+  if (c.w_dtype == MOE_E4M3) {
+    const size_t n = E + S, HB = H / 128, IB = I / 128;
+    // 128x1 operands: each expert's rows rounded up to 128
+    const size_t rcap = 128 * size_t(moe::f8_max_row_tiles(int(T), int(K), int(E), int(S)));
+    B.xst = take(rows * H * 2);
+    B.f32a = take(rows * I * 4);
+    B.f32b = take(rows * I * 4);
+    B.gq = take(rows * I);
+    B.gs = take(rows * IB * 4);
+    B.uq = take(rows * I);
+    B.us = take(rows * IB * 4);
+    B.dyq = take(rows * H);
+    B.dys = take(rows * HB * 4);
+    B.rowgate = take(TK * 4);
+    B.dg32 = take(rows * I * 4);
+    B.du32 = take(rows * I * 4);
+    B.dgq = take(rows * I);
+    B.dgs = take(rows * IB * 4);
+    B.duq = take(rows * I);
+    B.dus = take(rows * IB * 4);
+    B.dxst = take(rows * H * 2);
+    B.wgT = take(n * H * I);
+    B.wuT = take(n * H * I);
+    B.wdT = take(n * H * I);
+    B.sgT = take(n * HB * IB * 4);
+    B.suT = take(n * HB * IB * 4);
+    B.sdT = take(n * HB * IB * 4);
+    B.kp = take((n + 1) * 4);
+    B.dyT = take(rcap * H);
+    B.dysT = take(rcap / 128 * H * 4);
+    B.xT = take(rcap * H);
+    B.xsT = take(rcap / 128 * H * 4);
+    B.hT = take(rcap * I);
+    B.hsT = take(rcap / 128 * I * 4);
+    B.dgT = take(rcap * I);
+    B.dgsT = take(rcap / 128 * I * 4);
+    B.duT = take(rcap * I);
+    B.dusT = take(rcap / 128 * I * 4);
+    B.dg = take(TK * 4);
+    B.dl = take(TK * 4);
+    B.dlst = take(TK * 4);
+    B.wrt = take(E * H * 4);
+    B.dwrt = take(E * H * 4);
+    B.mt = take((n + 1) * 4);
+    B.total = off;
+    return B;
+  }
   B.xst = take(rows * H * 2);
   B.gst = take(rows * I * 2);
   B.ust = take(rows * I * 2);
@@ -404,7 +456,10 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
 // The backward stages its rows with 32-bit byte offsets: every staged-row
 // buffer must span less than 4 GiB.
 int validate_bwd(const moe_cfg* c, int64_t T) {
-  if (c->act_dtype != MOE_BF16 || c->w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (c->act_dtype != MOE_BF16 || (c->w_dtype != MOE_BF16 && c->w_dtype != MOE_E4M3))
+    return MOE_ERR_DTYPE;
+  // E4M3: a tile holds the weight-block scales of up to 128 K blocks
+  if (c->w_dtype == MOE_E4M3 && (c->hidden > 128 * 128 || c->inter > 128 * 128)) return MOE_ERR_SHAPE;
   if (c->hidden % 256 != 0 || c->inter % 256 != 0) return MOE_ERR_SHAPE;  // wgrad tiles of 256
   const int64_t rows = T * int64_t(c->topk + c->n_shared);
   if (rows * std::max<int64_t>(c->hidden, c->inter) * 2 >= (int64_t(1) << 32) - 256) return MOE_ERR_SHAPE;
@@ -438,6 +493,11 @@ int run_plain_gemm(const moe_cfg& c, int T, const bf16_t* a, const bf16_t* w, bf
   return moe::launch_tile_gemm(ta, false, max_mt, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
+                     const moe_experts* w, const bf16_t* dy, bf16_t* dx, float* dwr, float* dwg,
+                     float* dwu, float* dwd, void* ws, const BwdLayout& B, const RoutePtrs& r,
+                     hipStream_t st);
+
 int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, const float* bias,
                  const moe_experts* w, const bf16_t* dy, bf16_t* dx, float* dwr, float* dwg,
                  float* dwu, float* dwd, void* ws, const BwdLayout& B, hipStream_t st) {
@@ -446,6 +506,8 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   const RoutePtrs r = route_ptrs(nullptr, ws, L);
   int rc = run_route(c, T, x, wr, bias, r, ws, L, st);
   if (rc != MOE_OK) return rc;
+  if (c.w_dtype == MOE_E4M3)
+    return run_backward_fp8(c, T, x, wr, w, dy, dx, dwr, dwg, dwu, dwd, ws, B, r, st);
   moe::BwdArgs g{};
   g.x = x;
   g.perm = r.perm;
@@ -503,6 +565,139 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   MOE_TRY(timed(K_BWD_DH, st, [&] { return stage(4); }));
   MOE_TRY(timed(K_BWD_DX, st, [&] { return stage(5); }));
   MOE_TRY(timed(K_BWD_WGRAD, st, [&] { return stage(6); }));
+  MOE_TRY(timed(K_BWD_ROUTER, st, [&]() -> hipError_t {
+    hipError_t err = stage(7);
+    return err != hipSuccess ? err : stage(8);
+  }));
+  return MOE_OK;
+}
+
+// E4M3 weights: every expert GEMM of the backward in E4M3 (bwd_fp8_kernels.hip);
+// routing, gate gradients, dW_r and dx as on the bf16 path.
+int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
+                     const moe_experts* w, const bf16_t* dy, bf16_t* dx, float* dwr, float* dwg,
+                     float* dwu, float* dwd, void* ws, const BwdLayout& B, const RoutePtrs& r,
+                     hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
+  const Layout& L = B.f;
+  moe::BwdArgs8 q{};
+  q.x = x;
+  q.dy = dy;
+  q.perm = r.perm;
+  q.counts = r.counts;
+  q.offsets = r.offsets;
+  q.slot = r.slot;
+  q.gate = r.gate;
+  q.xq = at<uint8_t>(ws, L.xq);
+  q.xs = at<float>(ws, L.xs);
+  q.w_gate = static_cast<const uint8_t*>(w->w_gate);
+  q.w_up = static_cast<const uint8_t*>(w->w_up);
+  q.w_down = static_cast<const uint8_t*>(w->w_down);
+  q.s_gate = w->s_gate;
+  q.s_up = w->s_up;
+  q.s_down = w->s_down;
+  q.wgT = at<uint8_t>(ws, B.wgT);
+  q.wuT = at<uint8_t>(ws, B.wuT);
+  q.wdT = at<uint8_t>(ws, B.wdT);
+  q.sgT = at<float>(ws, B.sgT);
+  q.suT = at<float>(ws, B.suT);
+  q.sdT = at<float>(ws, B.sdT);
+  q.f32a = at<float>(ws, B.f32a);
+  q.f32b = at<float>(ws, B.f32b);
+  q.gq = at<uint8_t>(ws, B.gq);
+  q.gs = at<float>(ws, B.gs);
+  q.uq = at<uint8_t>(ws, B.uq);
+  q.us = at<float>(ws, B.us);
+  q.hq = at<uint8_t>(ws, L.hst);
+  q.hs = at<float>(ws, L.hs);
+  q.dyq = at<uint8_t>(ws, B.dyq);
+  q.dys = at<float>(ws, B.dys);
+  q.rowgate = at<float>(ws, B.rowgate);
+  q.dg32 = at<float>(ws, B.dg32);
+  q.du32 = at<float>(ws, B.du32);
+  q.dgq = at<uint8_t>(ws, B.dgq);
+  q.dgs = at<float>(ws, B.dgs);
+  q.duq = at<uint8_t>(ws, B.duq);
+  q.dus = at<float>(ws, B.dus);
+  q.dxst = at<bf16_t>(ws, B.dxst);
+  q.mt = at<int32_t>(ws, B.mt);
+  q.kp = at<int32_t>(ws, B.kp);
+  q.dyT = at<uint8_t>(ws, B.dyT);
+  q.dysT = at<float>(ws, B.dysT);
+  q.xT = at<uint8_t>(ws, B.xT);
+  q.xsT = at<float>(ws, B.xsT);
+  q.hT = at<uint8_t>(ws, B.hT);
+  q.hsT = at<float>(ws, B.hsT);
+  q.dgT = at<uint8_t>(ws, B.dgT);
+  q.dgsT = at<float>(ws, B.dgsT);
+  q.duT = at<uint8_t>(ws, B.duT);
+  q.dusT = at<float>(ws, B.dusT);
+  q.dw_gate = dwg;
+  q.dw_up = dwu;
+  q.dw_down = dwd;
+  q.E = E;
+  q.n_exp = E + S;
+  q.T = T;
+  q.TK = T * K;
+  q.K = K;
+  q.H = H;
+  q.I = I;
+  // the bf16 row kernels shared with the bf16 path
+  moe::BwdArgs g{};
+  g.x = x;
+  g.perm = r.perm;
+  g.counts = r.counts;
+  g.offsets = r.offsets;
+  g.mt = at<int32_t>(ws, B.mt);
+  g.xst = at<bf16_t>(ws, B.xst);
+  g.yst = at<bf16_t>(ws, L.yst);
+  g.dyst = nullptr;  // the output gradients are quantised from float32 instead
+  g.dxst = q.dxst;
+  g.dg = at<float>(ws, B.dg);
+  g.dl = at<float>(ws, B.dl);
+  g.dlst = at<float>(ws, B.dlst);
+  g.wrt = at<float>(ws, B.wrt);
+  g.dwrt = at<float>(ws, B.dwrt);
+  g.E = E;
+  g.n_exp = E + S;
+  g.T = T;
+  g.TK = T * K;
+  g.K = K;
+  g.H = H;
+  g.I = I;
+  const float* P = at<float>(ws, L.P);
+  const int ks = moe::router_partials(T, H, E, true);
+  auto stage = [&](int s) {
+    return moe::launch_backward_kernels(g, P, ks, r.idx, r.slot, r.gate, wr, dy, dx, dwr, st, s);
+  };
+  auto stage8 = [&](int s) { return moe::launch_backward_fp8(q, st, s); };
+  MOE_TRY(timed(K_BWD_WTRANS, st, [&] { return stage8(0); }));
+  // recompute: Q(x), G and U cached in E4M3, H, Y (the forward's down GEMM)
+  MOE_TRY(timed(K_BWD_RECOMPUTE, st, [&]() -> hipError_t {
+    hipError_t err;
+    if ((err = stage8(1)) != hipSuccess) return err;
+    if ((err = moe::launch_quant_1x128(x, T, H, at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), st)) !=
+        hipSuccess)
+      return err;
+    if ((err = stage8(2)) != hipSuccess) return err;
+    const int bm = moe::kTileM8;
+    const int max_mt = (T * K + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
+    moe::TileArgs8 ta{q.hq, q.hs, q.w_down, nullptr, q.s_down, nullptr, nullptr, g.yst, nullptr,
+                      r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_start), E, E + S, T, T * K,
+                      H, I};
+    if ((err = moe::launch_tile_gemm_fp8(ta, false, max_mt, st)) != hipSuccess) return err;
+    return stage(0);  // x in staged-row order (for dW_r)
+  }));
+  MOE_TRY(timed(K_BWD_COMBINE, st, [&]() -> hipError_t {
+    hipError_t err;
+    if ((err = stage(2)) != hipSuccess) return err;  // gate gradients
+    if ((err = stage(3)) != hipSuccess) return err;  // router backward
+    return stage8(3);                                // Q(dY)
+  }));
+  MOE_TRY(timed(K_BWD_DH, st, [&] { return stage8(4); }));
+  MOE_TRY(timed(K_BWD_DX, st, [&] { return stage8(5); }));
+  MOE_TRY(timed(K_BWD_RETILE, st, [&] { return stage8(6); }));
+  MOE_TRY(timed(K_BWD_WGRAD, st, [&] { return stage8(7); }));
   MOE_TRY(timed(K_BWD_ROUTER, st, [&]() -> hipError_t {
     hipError_t err = stage(7);
     return err != hipSuccess ? err : stage(8);
@@ -636,6 +831,8 @@ int moe_backward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_ro
       dw_down == nullptr)
     return MOE_ERR_NULL;
   if (w->w_gate == nullptr || w->w_up == nullptr || w->w_down == nullptr) return MOE_ERR_NULL;
+  if (cfg->w_dtype == MOE_E4M3 && (w->s_gate == nullptr || w->s_up == nullptr || w->s_down == nullptr))
+    return MOE_ERR_NULL;
   const BwdLayout B = make_bwd_layout(*cfg, T);
   if (ws == nullptr || ws_bytes < B.total) return MOE_ERR_WORKSPACE;
   if ((rc = check_device()) != MOE_OK) return rc;

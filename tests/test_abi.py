@@ -195,12 +195,18 @@ def test_backward_argument_checks():
     big = ctypes.c_size_t(1 << 40)
     n = L.moe_backward_workspace_bytes(ctypes.byref(c), 8192)
     assert n > L.moe_workspace_bytes(ctypes.byref(c), 8192) > 0
-    # bf16 activations and weights only
-    for kw in (dict(act_dtype=moe.F32, w_dtype=moe.F32), dict(w_dtype=moe.E4M3)):
-        cc = _v3(**kw)
-        assert L.moe_backward_workspace_bytes(ctypes.byref(cc), 256) == 0
-        assert L.moe_backward(ctypes.byref(cc), 256, one, one, one, ctypes.byref(ex), one, one, one,
-                              one, one, one, one, big, None) == -3
+    # bf16 activations with bf16 or E4M3 weights
+    cc = _v3(act_dtype=moe.F32, w_dtype=moe.F32)
+    assert L.moe_backward_workspace_bytes(ctypes.byref(cc), 256) == 0
+    assert L.moe_backward(ctypes.byref(cc), 256, one, one, one, ctypes.byref(ex), one, one, one,
+                          one, one, one, one, big, None) == -3
+    c8 = _v3(w_dtype=moe.E4M3)
+    n8 = L.moe_backward_workspace_bytes(ctypes.byref(c8), 256)
+    # three transposed E4M3 copies of the 257 experts' weights at least
+    assert n8 > 3 * 257 * 7168 * 2048
+    # E4M3 weights need their block scales
+    assert L.moe_backward(ctypes.byref(c8), 256, one, one, one, ctypes.byref(ex), one, one, one,
+                          one, one, one, one, big, None) == -1
     # staged rows past 4 GiB of 32-bit offsets
     assert L.moe_backward(ctypes.byref(c), 40000, one, one, one, ctypes.byref(ex), one, one, one,
                           one, one, one, one, big, None) == -2
