@@ -236,9 +236,12 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
   const int M = MODE == 0 ? g.H : g.I;
   const int N = MODE == 0 ? g.I : g.H;
   const int tm = M / BG_M, tn = N / WG_N;
-  const int e = blockIdx.x / (tm * tn);
-  if (e >= g.n_exp) return;  // uniform
-  const int t = blockIdx.x - e * tm * tn;
+  // experts in reverse order: the shared experts' tiles, which contract over
+  // all T rows, start first instead of forming the launch's tail
+  const int eb = blockIdx.x / (tm * tn);
+  if (eb >= g.n_exp) return;  // uniform
+  const int e = g.n_exp - 1 - eb;
+  const int t = blockIdx.x - eb * tm * tn;
   const int mt = t / tn, ntile = t - mt * tn;
   const int m0 = mt * BG_M, n0 = ntile * WG_N;
   int row_base, cnt;
@@ -328,7 +331,8 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        out[size_t(r) * N + col] = acc[i][j][v];
+        // written once: non-temporal (16.6 -> 14.8 ms for the three launches at 8192 tokens)
+        __builtin_nontemporal_store(acc[i][j][v], out + size_t(r) * N + col);
       }
     }
 }
