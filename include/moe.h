@@ -219,9 +219,7 @@ int moe_balance_loss(const moe_cfg* cfg, int64_t T, int32_t seq_len, const void*
  * gradients dG, dU are quantised in 1x128 tiles for the data-gradient GEMMs;
  * the weight-gradient GEMMs, which contract over an expert's rows, take both
  * operands in 128x1 tiles (per column, 128 consecutive rows of the expert
- * from its first row).  Scales follow moe_quantize_1x128's rule.  The
- * weights are transposed into the workspace on every call (three E4M3 copies
- * of the weights, about 3 * (E+S) * H * I bytes).
+ * from its first row).  Scales follow moe_quantize_1x128's rule.
  * Every output is overwritten.  Sums over tokens and experts run in a fixed
  * order (deterministic).  Staged rows use 32-bit offsets: T * (K + S) *
  * max(H, I) * 2 must stay below 4 GiB, and H * I * 2 too (else MOE_ERR_SHAPE).

@@ -85,12 +85,6 @@ struct BwdArgs8 {
   const float* s_gate;
   const float* s_up;
   const float* s_down;
-  uint8_t* wgT;               // [E+S][H][I] transposed codes, scales [E+S][H/128][I/128]
-  uint8_t* wuT;
-  uint8_t* wdT;               // [E+S][I][H], scales [E+S][I/128][H/128]
-  float* sgT;
-  float* suT;
-  float* sdT;
   float* f32a;                // [rows][I] G, then dH
   float* f32b;                // [rows][I] U
   uint8_t* gq;                // cached SwiGLU input [rows][I], scales [rows][I/128]
@@ -129,9 +123,8 @@ struct BwdArgs8 {
 
 int f8_max_row_tiles(int T, int K, int E, int S);
 
-// One stage of the E4M3 backward: 0 transposed weights, 1 prefixes, 2 G, U
-// and H, 3 Q(dY), 4 dH and the SwiGLU backward, 5 dX, 6 the 128x1 operands,
-// 7 weight gradients.
+// One stage of the E4M3 backward: 1 prefixes, 2 G, U and H, 3 Q(dY), 4 dH and
+// the SwiGLU backward, 5 dX, 6 the 128x1 operands, 7 weight gradients.
 hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage);
 
 }  // namespace moe

@@ -21,11 +21,12 @@
 //   dW_down = Q'(dY)^T Q'(H), dW_gate = Q'(dG)^T Q'(x), dW_up = Q'(dU)^T Q'(x)
 //   with Q' the 128x1 tiles over each expert's rows.
 //
-// The GEMM operands must have K contiguous, so the weights are transposed
-// once per call (W_down^T [I][H], W_gate^T and W_up^T [H][I]; a 128x128
-// block's scale serves both layouts) and the 128x1 operands are written
-// transposed: per expert e, [C][Kp_e] codes with Kp_e = its rows rounded up to
-// 128 (zero codes past its last row) and [C][Kp_e / 128] scales.
+// The data-gradient GEMMs contract over the weights' slow dimension: their
+// weight operand is staged in LDS as it is stored ([K][N] k-rows) and read
+// with the transposing ds_read_b64_tr_b8.  The 128x1 operands of the weight
+// gradients are written transposed: per expert e, [C][Kp_e] codes with Kp_e =
+// its rows rounded up to 128 (zero codes past its last row) and [C][Kp_e/128]
+// scales.
 #include "bwd.h"
 #include "common.h"
 
@@ -42,8 +43,9 @@ namespace {
 // l / 16 + 4 of the 128-byte K block (the same K map on both sides).
 //
 // GROUP 0 (row-grouped): expert e's staged rows against its [N][K] weight
-//   matrix with 128x128 block scales, tiles over mt[] (128-row tiles);
-//   optionally A rows gathered through perm from a [T][K] matrix.
+//   matrix with 128x128 block scales ([N/128][K/128]), tiles over mt[]
+//   (128-row tiles); optionally A rows gathered through perm from a [T][K]
+//   matrix.  BN: the weight matrix is [K][N] with [K/128][N/128] scales.
 // GROUP 1 (K-grouped): expert e's [M][Kp_e] A against its [N][Kp_e] B, both
 //   with per-row scales; C is expert e's [M][N] float32 slice.
 // NSRC == 2: C = A0 B0 + A1 B1 (same shapes), one accumulator.
@@ -55,6 +57,9 @@ constexpr int F8_OP = F8_T * 128;               // code bytes of one operand's s
 constexpr int F8_STAGE = 2 * F8_OP + 2 * F8_T * 4;  // A, B codes; A, B scales
 constexpr int F8_CPW = F8_OP / 1024 / 4;        // 1 KB copies per operand and wave (4)
 
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+
 MOE_DEV void copy16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
 }
@@ -62,7 +67,7 @@ MOE_DEV void copy4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, voff, 0, 0, 0);
 }
 
-template <int GROUP, int NSRC, typename TO>
+template <int GROUP, int NSRC, typename TO, bool BN>
 __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[F8_NS * F8_STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -166,7 +171,9 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
     const int r = 8 * (F8_CPW * wave + i) + (lane >> 3);
     const uint32_t sw = uint32_t(((lane & 7) ^ (r & 7)) * 16);
     aoff[i] = a_row_ok(r) ? a_row(r) * a_rowb + sw : a_bytes;
-    boff[i] = uint32_t(n0 + r) * (GROUP == 0 ? uint32_t(g.K) : a_rowb) + sw;
+    // BN: tile row r is k-row r of the [K][N] matrix, bytes n0 .. n0 + 127
+    boff[i] = BN ? uint32_t(r) * uint32_t(g.N) + uint32_t(n0) + sw
+                 : uint32_t(n0 + r) * (GROUP == 0 ? uint32_t(g.K) : a_rowb) + sw;
   }
   // one 4-byte scale copy per wave: waves 0, 1: A scales of tile rows
   // 64 w + l; waves 2, 3: B scales of tile rows 64 (w - 2) + l (GROUP 1), or
@@ -183,9 +190,11 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
   if (GROUP == 0) {
 #pragma unroll
     for (int s = 0; s < NSRC; ++s) {
-      const float* p = bs_base(s) + (size_t)(n0 / 128) * KB;
+      // block (n0 / 128, kb) of [N/128][K/128] scales, or (kb, n0 / 128) of [K/128][N/128] (BN)
+      const float* p = bs_base(s) + (BN ? (size_t)(n0 / 128) : (size_t)(n0 / 128) * KB);
+      const int stride = BN ? g.N / 128 : 1;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) sbv[s][c] = p[min(64 * c + lane, KB - 1)];
+      for (int c = 0; c < 2; ++c) sbv[s][c] = p[(size_t)min(64 * c + lane, KB - 1) * stride];
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -199,7 +208,8 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
       copy16(s1 ? ar1 : ar0, aoff[i] + kb * 128u, st + 8 * (F8_CPW * wave + i) * 128);
 #pragma unroll
     for (int i = 0; i < F8_CPW; ++i)
-      copy16(s1 ? br1 : br0, boff[i] + kb * 128u, st + F8_OP + 8 * (F8_CPW * wave + i) * 128);
+      copy16(s1 ? br1 : br0, boff[i] + kb * (BN ? 128u * uint32_t(g.N) : 128u),
+             st + F8_OP + 8 * (F8_CPW * wave + i) * 128);
     copy4(bscale ? bsr : (s1 ? sr1 : sr0), soff + kb * 4u, st + 2 * F8_OP + sdst);
   };
 
@@ -216,6 +226,24 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
     const i32x4 lo = *reinterpret_cast<const i32x4*>(base + r * 128 + ((g4 ^ (r & 7)) << 4));
     const i32x4 hi = *reinterpret_cast<const i32x4*>(base + r * 128 + (((g4 + 4) ^ (r & 7)) << 4));
     return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+  // The same operand of columns c0 .. c0 + 15 from a stage of k-rows (128 k x
+  // 128 columns, chunk c of k-row r at position c ^ (r % 8)), by four
+  // ds_read_b64_tr_b8: in each 16-lane group, source lane s addresses 8 bytes
+  // of k-row kq + s/2 (columns c0 + 8 (s%2) ..), and lane d receives byte d%8
+  // of source lane 2 j + d/8 as its byte j, i.e. k-rows kq .. kq + 7 of
+  // column c0 + d.  Lane l's k-rows: 16 (l/16) .. + 15 and 64 + 16 (l/16) .. + 15.
+  auto frag_kn = [&](const uint8_t* base, int c0) {
+    const int s = lane & 15;
+    v2i32 q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = 16 * g4 + 64 * (i >> 1) + 8 * (i & 1) + (s >> 1);
+      const uint8_t* p = base + kr * 128 + ((((c0 >> 4) ^ (kr & 7))) << 4) + 8 * (s & 1);
+      q[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i32*)((__attribute__((address_space(3))) uint8_t*)p));
+    }
+    return i32x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
   };
 
   if (steps > 0) issue(0);
@@ -237,7 +265,7 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
     float sbj[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf[j] = frag(st + F8_OP, 64 * wn + 16 * j + c16);
+      bf[j] = BN ? frag_kn(st + F8_OP, 64 * wn + 16 * j) : frag(st + F8_OP, 64 * wn + 16 * j + c16);
       sbj[j] = GROUP == 0 ? sbb : scB[64 * wn + 16 * j + c16];
     }
 #pragma unroll
@@ -303,44 +331,6 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
 }
 
 // ---------------------------------------------------------------- small kernels
-
-// out[m][c][r] = in[m][r][c] for E4M3 codes, 64 x 64 tiles through LDS
-__global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __restrict__ in, int R,
-                                                           int C, uint8_t* __restrict__ out) {
-  __shared__ uint32_t tile[64][17];  // 64 rows x 64 bytes, padded
-  const size_t mo = (size_t)blockIdx.z * R * C;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, a = tid >> 2, q = tid & 3;
-  const u32x4 v = *reinterpret_cast<const u32x4*>(in + mo + (size_t)(r0 + a) * C + c0 + 16 * q);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tile[a][4 * q + i] = v[i];
-  __syncthreads();
-  // thread (column a, rows 16 q .. 16 q + 15)
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r = 16 * q + 4 * i + b;
-      w |= ((tile[r][a >> 2] >> (8 * (a & 3))) & 0xffu) << (8 * b);
-    }
-    o[i] = w;
-  }
-  *reinterpret_cast<u32x4*>(out + mo + (size_t)(c0 + a) * R + r0 + 16 * q) = o;
-}
-
-// out[m][cb][rb] = in[m][rb][cb] for n matrices of Rb x Cb block scales
-__global__ __launch_bounds__(256) void transpose_scales_kernel(const float* __restrict__ in,
-                                                               int Rb, int Cb, long long total,
-                                                               float* __restrict__ out) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const long long per = (long long)Rb * Cb;
-  const long long m = i / per;
-  const int rem = int(i - m * per), rb = rem / Cb, cb = rem - rb * Cb;
-  out[m * per + (long long)cb * Rb + rb] = in[i];
-}
 
 // mt[e]: prefix of 128-row tiles; kp[e]: prefix of rows rounded up to 128
 // (routed counts, then the shared experts' T rows)
@@ -639,10 +629,10 @@ __global__ __launch_bounds__(256) void retile_kernel(RetileArgs g) {
   if (q == 0) g.outs[(size_t)(g.kp[e] / 128) * C + (size_t)(c0 + c) * (kpe / 128) + rb] = scale;
 }
 
-template <int GROUP, int NSRC, typename TO>
+template <int GROUP, int NSRC, typename TO, bool BN = false>
 hipError_t launch_gemm(const F8GemmArgs& a, unsigned blocks, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((f8_gemm_kernel<GROUP, NSRC, TO>), dim3(blocks), dim3(F8_NT), 0, st, a);
+  hipLaunchKernelGGL((f8_gemm_kernel<GROUP, NSRC, TO, BN>), dim3(blocks), dim3(F8_NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -665,29 +655,6 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
   } while (0)
   auto last = [] { return hipGetLastError(); };
   switch (stage) {
-    case 0: {  // transposed weights and block scales
-      // grid (columns / 64, rows / 64, matrices)
-      hipLaunchKernelGGL(transpose_u8_kernel, dim3(I / 64, H / 64, n), dim3(256), 0, st, g.w_down,
-                         H, I, g.wdT);
-      F8_TRY(last());
-      hipLaunchKernelGGL(transpose_u8_kernel, dim3(H / 64, I / 64, n), dim3(256), 0, st, g.w_gate,
-                         I, H, g.wgT);
-      F8_TRY(last());
-      hipLaunchKernelGGL(transpose_u8_kernel, dim3(H / 64, I / 64, n), dim3(256), 0, st, g.w_up, I,
-                         H, g.wuT);
-      F8_TRY(last());
-      const long long ns = (long long)n * (H / 128) * (I / 128);
-      const dim3 sg(unsigned((ns + 255) / 256));
-      hipLaunchKernelGGL(transpose_scales_kernel, sg, dim3(256), 0, st, g.s_down, H / 128, I / 128,
-                         ns, g.sdT);
-      F8_TRY(last());
-      hipLaunchKernelGGL(transpose_scales_kernel, sg, dim3(256), 0, st, g.s_gate, I / 128, H / 128,
-                         ns, g.sgT);
-      F8_TRY(last());
-      hipLaunchKernelGGL(transpose_scales_kernel, sg, dim3(256), 0, st, g.s_up, I / 128, H / 128,
-                         ns, g.suT);
-      break;
-    }
     case 1:  // tile and padded-row prefixes
       hipLaunchKernelGGL(f8_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T, g.mt,
                          g.kp);
@@ -735,8 +702,8 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       F8GemmArgs a{};
       a.a0 = g.dyq;
       a.as0 = g.dys;
-      a.b0 = g.wdT;
-      a.bs0 = g.sdT;
+      a.b0 = g.w_down;  // [H][I]: k-rows of the contraction over H
+      a.bs0 = g.s_down;
       a.out = g.f32a;
       a.counts = g.counts;
       a.offsets = g.offsets;
@@ -747,7 +714,7 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       a.TK = g.TK;
       a.N = I;
       a.K = H;
-      F8_TRY((launch_gemm<0, 1, float>(a, mtiles * (I / F8_T), st)));
+      F8_TRY((launch_gemm<0, 1, float, true>(a, mtiles * (I / F8_T), st)));
       const long long ns = (long long)rows * (I / 128);
       hipLaunchKernelGGL(swiglu_bwd_fp8_kernel, slices_grid(ns), dim3(256), 0, st, g.f32a, g.gq,
                          g.gs, g.uq, g.us, ns, g.dg32, g.du32, g.dgq, g.dgs, g.duq, g.dus);
@@ -757,12 +724,12 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       F8GemmArgs a{};
       a.a0 = g.dgq;
       a.as0 = g.dgs;
-      a.b0 = g.wgT;
-      a.bs0 = g.sgT;
+      a.b0 = g.w_gate;  // [I][H]: k-rows of the contraction over I
+      a.bs0 = g.s_gate;
       a.a1 = g.duq;
       a.as1 = g.dus;
-      a.b1 = g.wuT;
-      a.bs1 = g.suT;
+      a.b1 = g.w_up;
+      a.bs1 = g.s_up;
       a.out = g.dxst;
       a.counts = g.counts;
       a.offsets = g.offsets;
@@ -773,7 +740,7 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       a.TK = g.TK;
       a.N = H;
       a.K = I;
-      F8_TRY((launch_gemm<0, 2, bf16_t>(a, mtiles * (H / F8_T), st)));
+      F8_TRY((launch_gemm<0, 2, bf16_t, true>(a, mtiles * (H / F8_T), st)));
       break;
     }
     case 6: {  // 128x1 operands of the weight gradients

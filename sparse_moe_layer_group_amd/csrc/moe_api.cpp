@@ -136,14 +136,14 @@ int check_device() {
 enum Slot {
   K_ROUTER = 0, K_SELECT, K_PERMUTE, K_GATEUP, K_DOWN, K_COMBINE, K_BIAS, K_QUANT, K_BAL,
   K_BWD_RECOMPUTE, K_BWD_COMBINE, K_BWD_DH, K_BWD_DX, K_BWD_WGRAD, K_BWD_ROUTER,
-  K_BWD_WTRANS, K_BWD_RETILE,
+  K_BWD_RETILE,
   K_NSLOTS
 };
 const char* const kSlotNames[K_NSLOTS] = {
     "router_logits", "select",        "permute",       "gemm_gate_up",  "gemm_down",
     "combine",       "bias_update",   "quantize",      "balance_loss",  "bwd_recompute",
     "bwd_combine",   "bwd_dgrad_down", "bwd_dgrad_gate_up", "bwd_wgrad", "bwd_router_dx",
-    "bwd_weight_transpose", "bwd_retile_128x1"};
+    "bwd_retile_128x1"};
 
 struct Prof {
   bool on = false;
@@ -375,7 +375,7 @@ struct BwdLayout {
   size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dl, dlst, wrt, dwrt, mt, total;
   // E4M3 weights
   size_t f32a, f32b, gq, gs, uq, us, dyq, dys, rowgate, dg32, du32, dgq, dgs, duq, dus;
-  size_t wgT, wuT, wdT, sgT, suT, sdT, kp, dyT, dysT, xT, xsT, hT, hsT, dgT, dgsT, duT, dusT;
+  size_t kp, dyT, dysT, xT, xsT, hT, hsT, dgT, dgsT, duT, dusT;
 };
 
 BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
@@ -410,12 +410,6 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
     B.duq = take(rows * I);
     B.dus = take(rows * IB * 4);
     B.dxst = take(rows * H * 2);
-    B.wgT = take(n * H * I);
-    B.wuT = take(n * H * I);
-    B.wdT = take(n * H * I);
-    B.sgT = take(n * HB * IB * 4);
-    B.suT = take(n * HB * IB * 4);
-    B.sdT = take(n * HB * IB * 4);
     B.kp = take((n + 1) * 4);
     B.dyT = take(rcap * H);
     B.dysT = take(rcap / 128 * H * 4);
@@ -596,12 +590,6 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
   q.s_gate = w->s_gate;
   q.s_up = w->s_up;
   q.s_down = w->s_down;
-  q.wgT = at<uint8_t>(ws, B.wgT);
-  q.wuT = at<uint8_t>(ws, B.wuT);
-  q.wdT = at<uint8_t>(ws, B.wdT);
-  q.sgT = at<float>(ws, B.sgT);
-  q.suT = at<float>(ws, B.suT);
-  q.sdT = at<float>(ws, B.sdT);
   q.f32a = at<float>(ws, B.f32a);
   q.f32b = at<float>(ws, B.f32b);
   q.gq = at<uint8_t>(ws, B.gq);
@@ -671,7 +659,6 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
     return moe::launch_backward_kernels(g, P, ks, r.idx, r.slot, r.gate, wr, dy, dx, dwr, st, s);
   };
   auto stage8 = [&](int s) { return moe::launch_backward_fp8(q, st, s); };
-  MOE_TRY(timed(K_BWD_WTRANS, st, [&] { return stage8(0); }));
   // recompute: Q(x), G and U cached in E4M3, H, Y (the forward's down GEMM)
   MOE_TRY(timed(K_BWD_RECOMPUTE, st, [&]() -> hipError_t {
     hipError_t err;

@@ -202,8 +202,7 @@ def test_backward_argument_checks():
                           one, one, one, one, big, None) == -3
     c8 = _v3(w_dtype=moe.E4M3)
     n8 = L.moe_backward_workspace_bytes(ctypes.byref(c8), 256)
-    # three transposed E4M3 copies of the 257 experts' weights at least
-    assert n8 > 3 * 257 * 7168 * 2048
+    assert n8 > L.moe_workspace_bytes(ctypes.byref(c8), 256) > 0
     # E4M3 weights need their block scales
     assert L.moe_backward(ctypes.byref(c8), 256, one, one, one, ctypes.byref(ex), one, one, one,
                           one, one, one, one, big, None) == -1
