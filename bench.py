@@ -39,18 +39,23 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 # whose digest is recorded; after any change to them traffic reads null.
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
-MEASURED_TRAFFIC = {         # workload -> gemm_gate_up counters per launch
-    "decode": {"src_sha256": "f2b5447817cca990eadef93fc9e9451701b7155f534b28d3d3712356d48af261",
-               "fetch_kib": 8153701.1, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "ebb28573addc9f755a5e58341d54c853f8c77c88e60ed23180e0a7b9011d83ec",
-                "fetch_kib": 12321364.2, "write_kib": 294912.1},
+MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
+    "decode": {"src_sha256": "8dd5aaaaffd2786e84b5e04229af6c7e75929231a8b424762f4f3e627d5cadcd",
+              "fetch_kib": 8153178.8, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "c998abb2d7788ddc9bdd1f7c0962c155463a757ae0ecf2cc546486e08d66e6fc",
+               "fetch_kib": 12183248.9, "write_kib": 294912.0},
+    "backward_prefill_bf16": {"src_sha256": "04e3865690c92673947b1772131e3f340583d38d03f6b6845e543d68360dc859",
+                             "fetch_kib": 8766600.5, "write_kib": 44215682.1},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
 KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
                   "prefill": _COMMON_SOURCES + ("tile_gemm.hip",),
                   "skew": _COMMON_SOURCES + ("stream_gemm.hip", "tile_gemm.hip"),
-                  "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",)}
+                  "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",),
+                  # backward: the weight-gradient stage (three launches per call)
+                  "backward_prefill_bf16": _COMMON_SOURCES + ("bwd.h", "bwd_kernels.hip"),
+                  "backward_prefill_e4m3": _COMMON_SOURCES + ("bwd.h", "bwd_fp8_kernels.hip")}
 
 
 def log(msg):
@@ -66,7 +71,9 @@ def kernel_sources_sha256(workload):
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch of gemm_gate_up, or None when not measured for the current sources."""
+    """HBM bytes per launch of the roofline's kernel (gemm_gate_up; the backward's
+    three weight-gradient launches together), or None when not measured for the
+    current sources."""
     t = MEASURED_TRAFFIC.get(workload)
     if not t or not COPY_CALIBRATION or t["src_sha256"] != kernel_sources_sha256(workload):
         return None
@@ -383,7 +390,8 @@ def bench_backward(args, np, torch, moe, S):
     wg_flops = 3 * 2 * rows * H * I
     roofline = {"bound": "hbm", "achieved": round(wg_bytes / wg_s / 1e9, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(wg_bytes / wg_s / 1e9 / HBM_PEAK_GBS, 4),
-                "traffic": None, "kernel": "bwd_wgrad (dW_down, dW_gate, dW_up launches)",
+                "traffic": measured_traffic(f"backward_{args.backward_shape}_{c.w_dtype}"),
+                "kernel": "bwd_wgrad (dW_down, dW_gate, dW_up launches)",
                 "kernel_us": round(wg_s * 1e6, 2), "alg_bytes_per_launch": int(wg_bytes),
                 "alg_flops_per_launch": int(wg_flops),
                 "mfma_frac": round(wg_flops / wg_s / 1e12 / mfma_peak, 4)}
