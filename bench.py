@@ -47,6 +47,13 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
     "backward_prefill_bf16": {"src_sha256": "04e3865690c92673947b1772131e3f340583d38d03f6b6845e543d68360dc859",
                              "fetch_kib": 8766600.5, "write_kib": 44215682.1},
 }
+# MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
+# SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
+# busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
+MEASURED_MFMA = {
+    "prefill": {"src_sha256": "c998abb2d7788ddc9bdd1f7c0962c155463a757ae0ecf2cc546486e08d66e6fc",
+                "busy": 0.572, "clock_ghz": 1.56, "executed_bf16_tflop": 4.560},
+}
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
 KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
@@ -79,6 +86,14 @@ def measured_traffic(workload):
         return None
     return int(t["fetch_kib"] * COPY_CALIBRATION["fetch_bytes_per_kib"] +
                t["write_kib"] * COPY_CALIBRATION["write_bytes_per_kib"])
+
+
+def measured_mfma(workload):
+    """MFMA busy-cycle counters of gemm_gate_up, or None when not measured for the current sources."""
+    t = MEASURED_MFMA.get(workload)
+    if not t or t["src_sha256"] != kernel_sources_sha256(workload):
+        return None
+    return {k: v for k, v in t.items() if k != "src_sha256"}
 
 
 def copy_calibration(reps=5, nbytes=1 << 30):
@@ -286,6 +301,8 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "gemm_gate_up", "kernel_us": round(gu_s * 1e6, 2),
                 "alg_bytes_per_launch": int(gu_bytes), "alg_flops_per_launch": int(gu_flops)}
+    if bound == "mfma":
+        roofline["mfma_counters"] = measured_mfma(c.name)
     layer = {"ms": round(ms_step, 4), "alg_bytes": int(layer_bytes), "alg_flops": int(layer_flops),
              "hbm_frac": round(layer_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
              "mfma_frac": round(layer_flops / (ms_step / 1e3) / 1e12 /
