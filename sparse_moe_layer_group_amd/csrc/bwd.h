@@ -34,6 +34,7 @@ struct BwdArgs {
   float* dw_up;               // [E+S][I][H] float32 out
   float* dw_down;             // [E+S][H][I] float32 out
   int E, n_exp, T, TK, K, H, I;
+  int wg_xcd;                 // weight-gradient tiles in XCD-contiguous order
 };
 
 int bwd_max_row_tiles(int T, int K, int E, int S);
@@ -66,6 +67,7 @@ struct F8GemmArgs {
   const int32_t* mt;       // [n_exp+1] prefix of 128-row tiles
   const int32_t* kp;       // [n_exp+1] prefix of rows rounded up to 128
   int E, n_exp, T, TK, M, N, K;
+  int xcd;                 // K grouping: routed tiles in XCD-contiguous order
 };
 
 // Buffers of the E4M3 backward; rows are staged rows.

@@ -109,11 +109,23 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
   } else {
     const int nM = g.M / F8_T, nN = g.N / F8_T;
     // experts in reverse order: the shared experts' tiles, which contract
-    // over all T rows, start first instead of forming the launch's tail
-    const int eb = blockIdx.x / (nM * nN);
+    // over all T rows, start first instead of forming the launch's tail.
+    // With g.xcd (decode-sized batches) the routed experts' tiles go to the
+    // XCDs (workgroup b runs on XCD b % 8) in contiguous eighths, so each XCD
+    // writes a contiguous eighth of the gradients; the shared tiles' count is
+    // a multiple of 8 and the launch holds 8 ceil(routed tiles / 8) slots.
+    const int per_e = nM * nN, sh_tiles = (g.n_exp - g.E) * per_e;
+    int task = blockIdx.x;
+    if (g.xcd && task >= sh_tiles) {
+      const int b = task - sh_tiles, rt = g.E * per_e, per = (rt + 7) >> 3;
+      const int j = b >> 3;
+      task = sh_tiles + (b & 7) * per + j;
+      if (j >= per || task >= sh_tiles + rt) return;  // uniform
+    }
+    const int eb = task / per_e;
     if (eb >= g.n_exp) return;
     e = g.n_exp - 1 - eb;
-    const int rem = blockIdx.x - eb * nM * nN;
+    const int rem = task - eb * per_e;
     m0 = (rem / nN) * F8_T;
     n0 = (rem % nN) * F8_T;
     rows = F8_T;
@@ -793,6 +805,9 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       a.n_exp = n;
       a.T = T;
       a.TK = g.TK;
+      a.xcd = int64_t(T) * K <= int64_t(64) * E;  // decode-sized: at most 64 rows per expert
+      const unsigned per_e = unsigned((H / F8_T) * (I / F8_T));
+      const unsigned wtiles = per_e * unsigned(S) + 8 * ((per_e * unsigned(E) + 7) / 8);
       // dW_down [H][I] = Q'(dY)^T Q'(H)
       a.a0 = g.dyT;
       a.as0 = g.dysT;
@@ -801,7 +816,7 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       a.out = g.dw_down;
       a.M = H;
       a.N = I;
-      F8_TRY((launch_gemm<1, 1, float>(a, unsigned(n * (H / F8_T) * (I / F8_T)), st)));
+      F8_TRY((launch_gemm<1, 1, float>(a, wtiles, st)));
       // dW_gate, dW_up [I][H] = Q'(dG)^T Q'(x), Q'(dU)^T Q'(x)
       a.M = I;
       a.N = H;
@@ -810,11 +825,11 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       a.a0 = g.dgT;
       a.as0 = g.dgsT;
       a.out = g.dw_gate;
-      F8_TRY((launch_gemm<1, 1, float>(a, unsigned(n * (H / F8_T) * (I / F8_T)), st)));
+      F8_TRY((launch_gemm<1, 1, float>(a, wtiles, st)));
       a.a0 = g.duT;
       a.as0 = g.dusT;
       a.out = g.dw_up;
-      F8_TRY((launch_gemm<1, 1, float>(a, unsigned(n * (H / F8_T) * (I / F8_T)), st)));
+      F8_TRY((launch_gemm<1, 1, float>(a, wtiles, st)));
       break;
     }
     default:

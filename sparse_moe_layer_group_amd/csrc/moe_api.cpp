@@ -535,6 +535,7 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   g.K = K;
   g.H = H;
   g.I = I;
+  g.wg_xcd = int64_t(T) * K <= int64_t(64) * E;  // decode-sized: at most 64 rows per expert
   const float* P = at<float>(ws, L.P);
   const int ks = moe::router_partials(T, H, E, true);
   auto stage = [&](int s) {
