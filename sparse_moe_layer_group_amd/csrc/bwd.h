@@ -95,6 +95,7 @@ struct BwdArgs8 {
   float* us;
   uint8_t* hq;                // H for the down GEMM [rows][I], scales [rows][I/128]
   float* hs;
+  bf16_t* yst;                // [rows][H] recomputed expert outputs
   uint8_t* dyq;               // [rows][H], scales [rows][H/128]
   float* dys;
   float* rowgate;             // [T*K] gate of each routed staged row
@@ -125,8 +126,8 @@ struct BwdArgs8 {
 
 int f8_max_row_tiles(int T, int K, int E, int S);
 
-// One stage of the E4M3 backward: 1 prefixes, 2 G, U and H, 3 Q(dY), 4 dH and
-// the SwiGLU backward, 5 dX, 6 the 128x1 operands, 7 weight gradients.
+// One stage of the E4M3 backward: 1 prefixes, 2 G, U, H and Y, 3 Q(dY), 4 dH
+// and the SwiGLU backward, 5 dX, 6 the 128x1 operands, 7 weight gradients.
 hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage);
 
 }  // namespace moe

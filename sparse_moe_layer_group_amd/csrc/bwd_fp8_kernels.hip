@@ -14,7 +14,8 @@
 // Steps (rows are staged rows: routed experts in expert order, then the
 // shared expert's T rows):
 //   G = Q(x) W_gate^T, U = Q(x) W_up^T (float32), cached as Q(G), Q(U);
-//   H = SiLU(Q(G)) Q(U), quantised 1x128 for the down GEMM that recomputes Y;
+//   H = SiLU(Q(G)) Q(U), quantised 1x128 for the down GEMM that recomputes Y
+//   (with the same grouped GEMM);
 //   dY = g dy, quantised 1x128;   dH = Q(dY) W_down;
 //   dG = dH Q(U) SiLU'(Q(G)), dU = dH SiLU(Q(G)) (float32), quantised 1x128;
 //   dX = Q(dG) W_gate + Q(dU) W_up;
@@ -671,7 +672,7 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       hipLaunchKernelGGL(f8_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T, g.mt,
                          g.kp);
       break;
-    case 2: {  // G, U (float32) -> cached Q(G), Q(U); H -> Q(H)
+    case 2: {  // G, U (float32) -> cached Q(G), Q(U); H -> Q(H); Y
       F8GemmArgs a{};
       a.a0 = g.xq;
       a.as0 = g.xs;
@@ -702,6 +703,17 @@ hipError_t launch_backward_fp8(const BwdArgs8& g, hipStream_t st, int stage) {
       F8_TRY(last());
       hipLaunchKernelGGL(swiglu_fp8_kernel, slices_grid(ns), dim3(256), 0, st, g.gq, g.gs, g.uq,
                          g.us, ns, g.hq, g.hs);
+      F8_TRY(last());
+      // Y = Q(H) W_down^T, bf16 staged rows (for the gate gradients)
+      a.a0 = g.hq;
+      a.as0 = g.hs;
+      a.perm = nullptr;
+      a.b0 = g.w_down;
+      a.bs0 = g.s_down;
+      a.out = g.yst;
+      a.N = H;
+      a.K = I;
+      F8_TRY((launch_gemm<0, 1, bf16_t>(a, mtiles * (H / F8_T), st)));
       break;
     }
     case 3: {  // Q(dY) and the gate of each routed staged row

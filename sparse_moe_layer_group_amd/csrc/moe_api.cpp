@@ -599,6 +599,7 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
   q.us = at<float>(ws, B.us);
   q.hq = at<uint8_t>(ws, L.hst);
   q.hs = at<float>(ws, L.hs);
+  q.yst = at<bf16_t>(ws, L.yst);
   q.dyq = at<uint8_t>(ws, B.dyq);
   q.dys = at<float>(ws, B.dys);
   q.rowgate = at<float>(ws, B.rowgate);
@@ -660,7 +661,7 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
     return moe::launch_backward_kernels(g, P, ks, r.idx, r.slot, r.gate, wr, dy, dx, dwr, st, s);
   };
   auto stage8 = [&](int s) { return moe::launch_backward_fp8(q, st, s); };
-  // recompute: Q(x), G and U cached in E4M3, H, Y (the forward's down GEMM)
+  // recompute: Q(x), G and U cached in E4M3, H, Y
   MOE_TRY(timed(K_BWD_RECOMPUTE, st, [&]() -> hipError_t {
     hipError_t err;
     if ((err = stage8(1)) != hipSuccess) return err;
@@ -668,12 +669,6 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
         hipSuccess)
       return err;
     if ((err = stage8(2)) != hipSuccess) return err;
-    const int bm = moe::kTileM8;
-    const int max_mt = (T * K + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
-    moe::TileArgs8 ta{q.hq, q.hs, q.w_down, nullptr, q.s_down, nullptr, nullptr, g.yst, nullptr,
-                      r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_start), E, E + S, T, T * K,
-                      H, I};
-    if ((err = moe::launch_tile_gemm_fp8(ta, false, max_mt, st)) != hipSuccess) return err;
     return stage(0);  // x in staged-row order (for dW_r)
   }));
   MOE_TRY(timed(K_BWD_COMBINE, st, [&]() -> hipError_t {
