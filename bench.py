@@ -467,7 +467,8 @@ def cpu_baseline_backward(c, n_tok, x_dev, b_dev, dy_cpu):
     return {"value": round(n_tok / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 oracle backward{' (E4M3 emulation)' if f8 else ''} of the first "
                       f"{n_tok} tokens as their own batch "
-                      f"(dx, dW_r, and dW of the {len(touched)} experts they touch, shared included)"}
+                      f"(dx, dW_r, and dW of the {len(touched)} experts they touch, shared included)",
+            **host_info()}
 
 
 def router_partials(T, H, E):
@@ -513,6 +514,28 @@ def balance_loss_timing(moe, torch, cfg, c, x, wr, ws, dev, calls=5, alpha=1e-4)
             "loss_kernels_gbs": round(b_bytes / b_s / 1e9, 1)}
 
 
+def host_info():
+    """BLAS threads numpy's matmuls use and the host CPU's model string."""
+    try:
+        from threadpoolctl import threadpool_info
+        import numpy as np
+        np.ones((2, 2)) @ np.ones((2, 2))  # load the BLAS
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                   default=None)
+    except Exception:
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"blas_threads": blas, "cpu_model": model}
+
+
 def cpu_baseline(c, n_tok, x_dev, b_dev):
     """The float64 oracle on the first n_tok tokens' outputs (routing covers the whole batch)."""
     import numpy as np
@@ -549,7 +572,7 @@ def cpu_baseline(c, n_tok, x_dev, b_dev):
             "sample": f"float64 oracle forward: routing of all {c.T} tokens, expert outputs of the "
                       f"first {n_tok} tokens ({len(need)} experts' weights lifted to float64); "
                       f"input generation excluded; {dt:.1f}s",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), **host_info()}
 
 
 if __name__ == "__main__":
