@@ -315,6 +315,8 @@ def main():
     cpu = None
     if args.cpu_tokens > 0:
         cpu = cpu_baseline(c, args.cpu_tokens, x, b)
+        if skew is not None:
+            cpu["route_update_ms"] = cpu_route_update_ms(c, x, b)
 
     res = {
         "metric": "MoE-layer tokens/s on 1 MI355X; MFMA util (prefill) / HBM GB/s (decode)",
@@ -534,6 +536,23 @@ def host_info():
     except OSError:
         pass
     return {"blas_threads": blas, "cpu_model": model}
+
+
+def cpu_route_update_ms(c, x_dev, b_dev):
+    """The oracle's routing of one whole batch plus its bias update (one step of
+    the loss-free balancing loop), in ms; input generation excluded."""
+    import oracle as O
+    import synthetic as S
+    x64 = O.lift(x_dev.float().cpu())
+    wr64 = O.lift(S.gen_router(c, "cpu"))
+    b = b_dev.cpu().numpy()
+    t0 = time.perf_counter()
+    L, s, r, p = O.route(x64, wr64, b, n_groups=c.n_groups, topk_groups=c.topk_groups, topk=c.topk,
+                         group_topn=c.group_topn)
+    O.bias_update(b, p.counts, c.T, c.topk, c.gamma)
+    ms = (time.perf_counter() - t0) * 1e3
+    log(f"cpu baseline: oracle route + bias update of {c.T} tokens in {ms:.1f} ms")
+    return round(ms, 2)
 
 
 def cpu_baseline(c, n_tok, x_dev, b_dev):
