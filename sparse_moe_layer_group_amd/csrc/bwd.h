@@ -12,7 +12,8 @@ struct BwdArgs {
   const int32_t* perm;        // [T*K] token of each routed staged row
   const int32_t* counts;      // [E]
   const int32_t* offsets;     // [E+1]
-  int32_t* mt;                // [E+S+1] row-tile prefix of the dgrad GEMM
+  int32_t* mt;                // [E+S+1] prefix of 128-row tiles
+  int32_t* mtd;               // [E+S+1] prefix of the large-tile dgrad GEMM's row tiles, or null
   const bf16_t* w_gate;       // [E+S][I][H]
   const bf16_t* w_up;         // [E+S][I][H]
   const bf16_t* w_down;       // [E+S][H][I]

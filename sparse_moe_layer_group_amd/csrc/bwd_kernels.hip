@@ -84,6 +84,8 @@ MOE_DEV void expert_rows(const BwdArgs& g, int e, int& base, int& cnt) {
 }  // namespace
 
 // ---------------------------------------------------------------- dgrad GEMM
+// (128-row tiles, for decode-sized batches; dgrad_tile_kernel below serves
+// batches with 32 or more rows per expert.)
 // MODE 0: dH = dY W_down (K = hidden, N = inter); epilogue: SwiGLU backward,
 //         dG = dH * U * SiLU'(G), dU = dH * SiLU(G) from the staged G and U.
 // MODE 1: dX = dG W_gate + dU W_up (K = 2 x inter in two passes, N = hidden).
@@ -223,6 +225,220 @@ __global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
         }
       }
     }
+}
+
+// ---------------------------------------------------------------- dgrad GEMM, large tiles
+// The same products as dgrad_gemm_kernel on the forward tile GEMM's design:
+// tile 320 rows x 256 output columns, eight waves in 2 x 4 of 160 x 64 (5 x 2
+// MFMA blocks, 32-row blocks past the expert's count skipped per wave), K in
+// steps of 64 with two LDS stages.  Waves 0-3 copy only weight k-rows (2
+// k-rows of 256 columns per 1 KB copy), waves 4-7 only staged rows (8 rows of
+// 128 bytes per copy), and each waits only for its own copies.  A step's four
+// k16 slices: each slice's fragments are read among the previous slice's
+// MFMAs; after slice 2's MFMAs a wave waits for its copies of the next step
+// and its LDS reads, the workgroup barriers, the copies two steps ahead go
+// into the stage just finished, and slice 0 of the next step is read among
+// slice 3's MFMAs.  Weight fragments come through ds_read_b64_tr_b16.
+namespace {
+constexpr int DT_M = 320, DT_N = 256, DT_K = 64;
+constexpr int DT_MBW = DT_M / 64;                   // 32-row MFMA blocks per wave (5)
+constexpr int DT_WN = 4, DT_NWAVE = 8, DT_NT = 64 * DT_NWAVE;
+constexpr int DT_NJ = DT_N / DT_WN / 32;            // 32-column MFMA blocks per wave (2)
+constexpr int DT_ASTAGE = DT_M * DT_K, DT_BSTAGE = DT_K * DT_N;  // bf16 elements per stage
+constexpr int DT_ACP = DT_M / 8 / 4;                // 1 KB copies per row wave per step (10)
+constexpr int DT_BCP = DT_K / 2 / 4;                // ... per weight wave (8)
+static_assert(DT_ACP * 2 < 64 && DT_BCP * 2 < 64, "vmcnt field is 6 bits");
+
+MOE_DEV bf16x8 dt_afrag(const bf16_t* base, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(base + row * DT_K + ((chunk ^ (row & 7)) << 3));
+}
+}  // namespace
+
+int dgrad_tile_rows() { return DT_M; }
+size_t dgrad_tile_lds_bytes() { return size_t(2 * (DT_ASTAGE + DT_BSTAGE)) * sizeof(bf16_t); }
+
+template <int MODE>
+__global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t dsm[];
+  bf16_t* As = dsm;                    // [2][DT_M][DT_K]
+  bf16_t* Bs = dsm + 2 * DT_ASTAGE;    // [2][DT_K][DT_N]
+  const int N = MODE == 0 ? g.I : g.H;           // output columns
+  const int Kp = MODE == 0 ? g.H : g.I;          // K of one pass
+  const int n_nt = N / DT_N;
+  const int n_tasks = g.mtd[g.n_exp] * n_nt;
+  const int task = blockIdx.x;
+  if (task >= n_tasks) return;  // uniform, before any barrier
+  int lo = 0, hi = g.n_exp - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.mtd[mid] * n_nt <= task) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int n_mt = g.mtd[e + 1] - g.mtd[e];
+  const int local = task - g.mtd[e] * n_nt;
+  const int nt = local / n_mt, mtile = local - nt * n_mt;
+  int row_base, cnt;
+  expert_rows(g, e, row_base, cnt);
+  const int m0 = mtile * DT_M, n0 = nt * DT_N;
+  const int rows = min(DT_M, cnt - m0);
+  const int nk1 = Kp / DT_K;
+  const int nk = MODE == 0 ? nk1 : 2 * nk1;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / DT_WN, wn = wave % DT_WN;
+  const bool copies_b = wave < 4;
+  const int cw = wave & 3;
+
+  const uint32_t total_rows = uint32_t(g.TK + (g.n_exp - g.E) * g.T);
+  __amdgpu_buffer_rsrc_t r0, r1;
+  uint32_t off[DT_ACP > DT_BCP ? DT_ACP : DT_BCP];
+  if (copies_b) {
+    const size_t wsz = size_t(Kp) * N;
+    r0 = buffer_rsrc((MODE == 0 ? g.w_down : g.w_gate) + size_t(e) * wsz, uint32_t(wsz * 2));
+    r1 = buffer_rsrc((MODE == 0 ? g.w_down : g.w_up) + size_t(e) * wsz, uint32_t(wsz * 2));
+#pragma unroll
+    for (int i = 0; i < DT_BCP; ++i) {  // k-rows 2 (DT_BCP cw + i) + lane/32, chunk lane%32
+      const int kr = 2 * (DT_BCP * cw + i) + (lane >> 5);
+      off[i] = (uint32_t(kr) * uint32_t(N) + uint32_t(n0 + kswz(kr, lane & 31) * 8)) * 2u;
+    }
+  } else {
+    r0 = buffer_rsrc(MODE == 0 ? g.dyst : g.dgst, total_rows * uint32_t(Kp) * 2u);
+    r1 = buffer_rsrc(MODE == 0 ? g.dyst : g.dust, total_rows * uint32_t(Kp) * 2u);
+#pragma unroll
+    for (int i = 0; i < DT_ACP; ++i) {  // rows 8 (DT_ACP cw + i) + lane/8, position lane%8
+      const int r = 8 * (DT_ACP * cw + i) + (lane >> 3);
+      const int m = row_base + m0 + min(r, rows - 1);  // rows past the count re-read a valid row
+      off[i] = (uint32_t(m) * uint32_t(Kp) + uint32_t(((lane & 7) ^ (r & 7)) * 8)) * 2u;
+    }
+  }
+  auto copy_step = [&](int kt) {
+    const int k = min(kt, nk - 1);
+    const bool second = MODE == 1 && k >= nk1;
+    const uint32_t kk = uint32_t(second ? k - nk1 : k);
+    const __amdgpu_buffer_rsrc_t rs = second ? r1 : r0;
+    if (copies_b) {
+      bf16_t* d = Bs + (kt & 1) * DT_BSTAGE + 2 * DT_BCP * cw * DT_N;
+      const uint32_t ko = kk * uint32_t(DT_K) * uint32_t(N) * 2u;
+#pragma unroll
+      for (int i = 0; i < DT_BCP; ++i) copy16_to_lds(rs, off[i] + ko, d + 2 * i * DT_N);
+    } else {
+      bf16_t* d = As + (kt & 1) * DT_ASTAGE + 8 * DT_ACP * cw * DT_K;
+      const uint32_t ko = kk * uint32_t(DT_K) * 2u;
+#pragma unroll
+      for (int i = 0; i < DT_ACP; ++i) copy16_to_lds(rs, off[i] + ko, d + 8 * i * DT_K);
+    }
+  };
+
+  const int mrows = rows - wm * 32 * DT_MBW;
+  const int mact = __builtin_amdgcn_readfirstlane(mrows <= 0 ? 0 : min(DT_MBW, (mrows + 31) >> 5));
+  f32x16 acc[DT_MBW][DT_NJ];
+#pragma unroll
+  for (int i = 0; i < DT_MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < DT_NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int arow0 = wm * 32 * DT_MBW + (lane & 31);
+
+  auto mainloop = [&](auto mact_c) {
+    constexpr int MACT = decltype(mact_c)::value;
+    struct Frags { bf16x8 a[DT_MBW], b[DT_NJ]; };
+    auto rd = [&](Frags& f, int kt, int sl) {
+      const bf16_t* a = As + (kt & 1) * DT_ASTAGE;
+      const bf16_t* b = Bs + (kt & 1) * DT_BSTAGE;
+#pragma unroll
+      for (int j = 0; j < DT_NJ; ++j) f.b[j] = tr_frag<DT_N>(b, 16 * sl, wn * 64 + 32 * j, lane);
+#pragma unroll
+      for (int i = 0; i < MACT; ++i) f.a[i] = dt_afrag(a, arow0 + 32 * i, 2 * sl + (lane >> 5));
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+      for (int i = 0; i < MACT; ++i)
+#pragma unroll
+        for (int j = 0; j < DT_NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    // reads per slice: MACT row fragments and 2 DT_NJ transposed reads
+    auto interleave = [&]() {
+      static_assert(DT_NJ == 2, "two transposed weight fragments per slice");
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int k = 0; k < MACT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (MACT * DT_NJ > MACT + DT_NJ)
+        __builtin_amdgcn_sched_group_barrier(0x008, MACT * DT_NJ - MACT - DT_NJ, 0);
+    };
+    copy_step(0);
+    copy_step(1);
+    if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm(DT_BCP));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(DT_ACP));
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    rd(f0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      rd(f1, kt, 1);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      rd(f0, kt, 2);
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      rd(f1, kt, 3);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      copy_step(kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      rd(f0, kt + 1, 0);
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no copy left in flight
+  };
+  switch (mact) {
+    case 5: mainloop(std::integral_constant<int, 5>{}); break;
+    case 4: mainloop(std::integral_constant<int, 4>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    default: mainloop(std::integral_constant<int, 0>{}); break;
+  }
+
+  // epilogue.  32x32 accumulator v of lane l: row 8 (v/4) + 4 (l/32) + v%4, column l%32
+#pragma unroll
+  for (int i = 0; i < DT_MBW; ++i) {
+    if (i >= mact) continue;  // uniform
+#pragma unroll
+    for (int j = 0; j < DT_NJ; ++j) {
+      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 32 * DT_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r >= rows) continue;
+        const size_t o = size_t(row_base + m0 + r) * N + col;
+        const float d = acc[i][j][v];
+        if (MODE == 0) {
+          const float G = bf16_to_f32(g.gst[o]), U = bf16_to_f32(g.ust[o]);
+          const float sg = sigm(G);
+          g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
+          g.dust[o] = f32_to_bf16(d * G * sg);
+        } else {
+          g.dxst[o] = f32_to_bf16(d);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- wgrad GEMM
@@ -564,14 +780,14 @@ __global__ __launch_bounds__(256) void dx_kernel(const bf16_t* __restrict__ dxst
 // row-tile prefix of the dgrad GEMM: mt[e] = sum over experts before e of
 // ceil(rows / 128) (routed counts, then the shared experts' T rows)
 __global__ __launch_bounds__(64) void bwd_tile_prefix_kernel(const int32_t* __restrict__ counts,
-                                                             int E, int S, int T,
+                                                             int E, int S, int T, int tile,
                                                              int32_t* __restrict__ mt) {
   if (threadIdx.x != 0) return;
   int acc = 0;
   for (int e = 0; e < E + S; ++e) {
     mt[e] = acc;
     const int c = e < E ? counts[e] : T;
-    acc += (c + BG_M - 1) / BG_M;
+    acc += (c + tile - 1) / tile;
   }
   mt[E + S] = acc;
 }
@@ -581,6 +797,26 @@ __global__ __launch_bounds__(64) void bwd_tile_prefix_kernel(const int32_t* __re
 int bwd_max_row_tiles(int T, int K, int E, int S) {
   return (T * K + BG_M - 1) / BG_M + E + S * ((T + BG_M - 1) / BG_M);
 }
+
+namespace {
+int dgrad_max_tiles(int T, int K, int E, int S) {
+  return (T * K + DT_M - 1) / DT_M + E + S * ((T + DT_M - 1) / DT_M);
+}
+
+template <int MODE>
+hipError_t launch_dgrad_tile(const BwdArgs& g, unsigned blocks, hipStream_t st) {
+  static bool attr_set = false;
+  const size_t lds = dgrad_tile_lds_bytes();
+  if (!attr_set) {
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&dgrad_tile_kernel<MODE>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(dgrad_tile_kernel<MODE>, dim3(blocks), dim3(DT_NT), lds, st, g);
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, const int32_t* idx,
                                    const int32_t* slot, const float* gate, const float* w_router,
@@ -605,14 +841,21 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
       hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 255) / 256), dim3(256), 0, st, P, ks, idx,
                          slot, g.dg, T, E, K, g.dl, g.dlst);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-      hipLaunchKernelGGL(bwd_tile_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T,
+      hipLaunchKernelGGL(bwd_tile_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T, BG_M,
                          const_cast<int32_t*>(g.mt));
+      if (g.mtd != nullptr) {
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL(bwd_tile_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T,
+                           DT_M, g.mtd);
+      }
       break;
     case 4:  // dH = dY W_down with the SwiGLU backward
+      if (g.mtd != nullptr) return launch_dgrad_tile<0>(g, unsigned(dgrad_max_tiles(T, K, E, S) * (I / DT_N)), st);
       hipLaunchKernelGGL(dgrad_gemm_kernel<0>, dim3(unsigned(bwd_max_row_tiles(T, K, E, S) * (I / DG_N))),
                          dim3(BG_NT), 0, st, g);
       break;
     case 5:  // dX = dG W_gate + dU W_up
+      if (g.mtd != nullptr) return launch_dgrad_tile<1>(g, unsigned(dgrad_max_tiles(T, K, E, S) * (H / DT_N)), st);
       hipLaunchKernelGGL(dgrad_gemm_kernel<1>, dim3(unsigned(bwd_max_row_tiles(T, K, E, S) * (H / DG_N))),
                          dim3(BG_NT), 0, st, g);
       break;

@@ -372,7 +372,7 @@ int run_experts_fp8(const moe_cfg& c, int T, const bf16_t* x, const moe_experts*
 // then the backward's staged rows and per-assignment buffers.
 struct BwdLayout {
   Layout f;
-  size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dl, dlst, wrt, dwrt, mt, total;
+  size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dl, dlst, wrt, dwrt, mt, mtd, total;
   // E4M3 weights
   size_t f32a, f32b, gq, gs, uq, us, dyq, dys, rowgate, dg32, du32, dgq, dgs, duq, dus;
   size_t kp, dyT, dysT, xT, xsT, hT, hsT, dgT, dgsT, duT, dusT;
@@ -443,6 +443,7 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
   B.wrt = take(E * H * 4);
   B.dwrt = take(E * H * 4);
   B.mt = take((E + S + 1) * 4);
+  B.mtd = take((E + S + 1) * 4);
   B.total = off;
   return B;
 }
@@ -508,6 +509,9 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   g.counts = r.counts;
   g.offsets = r.offsets;
   g.mt = at<int32_t>(ws, B.mt);
+  // 320-row data-gradient tiles from 32 routed rows per expert on average
+  // (prefill: 4.29 + 7.07 -> 3.72 + 5.48 ms); 128-row tiles below (decode)
+  g.mtd = int64_t(T) * K >= int64_t(32) * E ? at<int32_t>(ws, B.mtd) : nullptr;
   g.w_gate = static_cast<const bf16_t*>(w->w_gate);
   g.w_up = static_cast<const bf16_t*>(w->w_up);
   g.w_down = static_cast<const bf16_t*>(w->w_down);
