@@ -40,19 +40,19 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
-    "decode": {"src_sha256": "8dd5aaaaffd2786e84b5e04229af6c7e75929231a8b424762f4f3e627d5cadcd",
-              "fetch_kib": 8153178.8, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "c998abb2d7788ddc9bdd1f7c0962c155463a757ae0ecf2cc546486e08d66e6fc",
-               "fetch_kib": 12183248.9, "write_kib": 294912.0},
-    "backward_prefill_bf16": {"src_sha256": "04e3865690c92673947b1772131e3f340583d38d03f6b6845e543d68360dc859",
-                             "fetch_kib": 8766600.5, "write_kib": 44215682.1},
+    "decode": {"src_sha256": "1548235720ad8555eb6f6ba41963e92d279bf399b54c926ff6e5ab3e38d1cb8a",
+              "fetch_kib": 8151080.2, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "87067b36c57a104b5b0fc9a56fe9a9822c02f2165b97d201c90f28d8c9b3d2c4",
+               "fetch_kib": 12180334.7, "write_kib": 294912.1},
+    "backward_prefill_bf16": {"src_sha256": "b72e7ab0c31f4704620ce90ffc2ad0838b110aee61a3554bbaf35212e4be5f1b",
+                             "fetch_kib": 8765728.9, "write_kib": 44216636.7},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "c998abb2d7788ddc9bdd1f7c0962c155463a757ae0ecf2cc546486e08d66e6fc",
-                "busy": 0.572, "clock_ghz": 1.56, "executed_bf16_tflop": 4.560},
+    "prefill": {"src_sha256": "87067b36c57a104b5b0fc9a56fe9a9822c02f2165b97d201c90f28d8c9b3d2c4",
+                "busy": 0.567, "clock_ghz": 1.56, "executed_bf16_tflop": 4.56},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
