@@ -41,18 +41,18 @@ COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buff
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
     "decode": {"src_sha256": "1548235720ad8555eb6f6ba41963e92d279bf399b54c926ff6e5ab3e38d1cb8a",
-              "fetch_kib": 8151080.2, "write_kib": 9216.0},
+              "fetch_kib": 8152847.6, "write_kib": 9216.0},
     "prefill": {"src_sha256": "87067b36c57a104b5b0fc9a56fe9a9822c02f2165b97d201c90f28d8c9b3d2c4",
-               "fetch_kib": 12180334.7, "write_kib": 294912.1},
-    "backward_prefill_bf16": {"src_sha256": "b72e7ab0c31f4704620ce90ffc2ad0838b110aee61a3554bbaf35212e4be5f1b",
-                             "fetch_kib": 8765728.9, "write_kib": 44216636.7},
+               "fetch_kib": 12193395.5, "write_kib": 294912.0},
+    "backward_prefill_bf16": {"src_sha256": "300f12aa2ed1c421c3e3d2ee62ada241ac861ab449ebe302d35019cfaf106525",
+                             "fetch_kib": 8764995.2, "write_kib": 44216125.6},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
     "prefill": {"src_sha256": "87067b36c57a104b5b0fc9a56fe9a9822c02f2165b97d201c90f28d8c9b3d2c4",
-                "busy": 0.567, "clock_ghz": 1.56, "executed_bf16_tflop": 4.56},
+                "busy": 0.58, "clock_ghz": 1.47, "executed_bf16_tflop": 4.56},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")

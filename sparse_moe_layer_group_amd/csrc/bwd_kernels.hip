@@ -11,14 +11,17 @@
 // rows offsets[e] .. offsets[e] + counts[e] - 1 in expert order (perm gives
 // their token ids), then the shared expert's T rows (row T*K + t is token t).
 //
-// GEMMs.  Two LDS-tiled grouped GEMMs on 32x32x16 bf16 MFMAs (K steps of 32,
-// four waves, three LDS stages filled two steps ahead by buffer_load ... lds
-// copies; tiles 128 x 256 with waves of 64 x 128):
+// GEMMs.  LDS-tiled grouped GEMMs on 32x32x16 bf16 MFMAs, operands copied
+// straight into LDS by buffer_load ... lds:
 //   - dgrad:  out[row][n] = sum_k A[row][k] B[k][n] over an expert's rows,
 //     A = staged rows (k contiguous), B = the expert's weight matrix read along
-//     its slow dimension (dH = dY W_down; dX = dG W_gate + dU W_up);
+//     its slow dimension (dH = dY W_down; dX = dG W_gate + dU W_up).
+//     dgrad_tile_kernel (32 or more rows per expert): 320 x 256 tiles, eight
+//     waves, K steps of 64 in two stages; dgrad_gemm_kernel (decode-sized
+//     batches): 128 x 256 tiles, four waves, K steps of 32 in three stages;
 //   - wgrad:  out[m][n] = sum over the expert's rows r of A[r][m] B[r][n]
-//     (dW_down = dY^T H, dW_gate = dG^T X, dW_up = dU^T X), float32 out.
+//     (dW_down = dY^T H, dW_gate = dG^T X, dW_up = dU^T X), float32 out;
+//     128 x 256 tiles, four waves, K steps of 32 rows in three stages.
 // Operands whose contraction index is their slow (row) dimension are staged in
 // LDS as "k-rows" in memory order and read with ds_read_b64_tr_b16: in each
 // group of 16 lanes, source lane s addresses 4 consecutive columns of k-row
