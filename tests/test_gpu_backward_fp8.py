@@ -75,7 +75,9 @@ def _fmt(rows, mats, wr):
             f"{np.median(mats):.2e} max {mats.max():.2e}; dW_r {wr:.2e}")
 
 
-@pytest.mark.parametrize("T", [300, 65, 1])
+# T=1200: 114-191 rows per routed expert, so every expert's 128x1 tiles span two
+# row blocks with a partial last one
+@pytest.mark.parametrize("T", [300, 65, 1, 1200])
 def test_fp8_backward_parity(T):
     c = S.get_config("mid_fp8", T=T)
     say(f"fp8 backward parity: mid_fp8 T={T}")
