@@ -27,6 +27,8 @@ struct BwdArgs {
   bf16_t* dust;               // [rows][I]
   bf16_t* dxst;               // [rows][H] expert input gradients
   float* dg;                  // [T*K] gate gradients
+  float* dgp;                 // [I/256][rows] per-tile row sums of dH * H (gate gradients
+                              // without recomputing Y), or null: dg from the recomputed Y
   float* dl;                  // [T*K] logit gradients of the chosen experts
   float* dlst;                // [T*K] the same per routed staged row
   float* wrt;                 // [E][H] W_r transposed
@@ -40,9 +42,10 @@ struct BwdArgs {
 
 int bwd_max_row_tiles(int T, int K, int E, int S);
 
-// One stage of the backward (0 gather x, 1 SwiGLU, 2 combine backward,
-// 3 router backward, 4 dH GEMM, 5 dX GEMM, 6 weight-gradient GEMMs,
-// 7 dW_r, 8 dx); P / ks: router partials and their count.
+// One stage of the backward (0 gather x, 1 SwiGLU, 2 combine backward and tile
+// prefixes, 3 router backward, 4 dH GEMM, 5 dX GEMM, 6 weight-gradient GEMMs,
+// 7 dW_r, 8 dx); P / ks: router partials and their count.  With dgp, stage 3
+// runs after stage 4.
 hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, const int32_t* idx,
                                    const int32_t* slot, const float* gate, const float* w_router,
                                    const bf16_t* dy, bf16_t* dx, float* dw_router, hipStream_t st,

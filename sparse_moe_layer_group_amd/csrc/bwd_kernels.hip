@@ -207,6 +207,11 @@ __global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   // epilogue.  32x32 accumulator v of lane l: row 8 (v/4) + 4 (l/32) + v%4, column l%32
+  float part[2][16];  // MODE 0 with g.dgp: this lane's sum of dH * H per row
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[i][v] = 0.f;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -223,11 +228,32 @@ __global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
           const float sg = sigm(G);
           g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
           g.dust[o] = f32_to_bf16(d * G * sg);
+          part[i][v] = fmaf(d, bf16_to_f32(g.hst[o]), part[i][v]);
         } else {
           g.dxst[o] = f32_to_bf16(d);
         }
       }
     }
+  if (MODE == 0 && g.dgp != nullptr) {
+    // row sums over the tile's 256 columns: 32 lanes of a half-wave (fixed
+    // butterfly), then the 2 waves along N through LDS in wave order
+    float* red = reinterpret_cast<float*>(smem);  // [2][BG_M]
+    __syncthreads();  // every wave is done with the stages
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float t = part[i][v];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) t += __shfl_xor(t, off, 32);
+        if ((lane & 31) == 0)
+          red[wn * BG_M + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = t;
+      }
+    __syncthreads();
+    if (tid < rows)
+      g.dgp[size_t(nt) * (g.TK + (g.n_exp - g.E) * g.T) + row_base + m0 + tid] =
+          red[tid] + red[BG_M + tid];
+  }
 }
 
 // ---------------------------------------------------------------- dgrad GEMM, large tiles
@@ -419,6 +445,11 @@ __global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
   }
 
   // epilogue.  32x32 accumulator v of lane l: row 8 (v/4) + 4 (l/32) + v%4, column l%32
+  float part[DT_MBW][16];  // MODE 0 with g.dgp: this lane's sum of dH * H per row
+#pragma unroll
+  for (int i = 0; i < DT_MBW; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) part[i][v] = 0.f;
 #pragma unroll
   for (int i = 0; i < DT_MBW; ++i) {
     if (i >= mact) continue;  // uniform
@@ -436,9 +467,38 @@ __global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
           const float sg = sigm(G);
           g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
           g.dust[o] = f32_to_bf16(d * G * sg);
+          part[i][v] = fmaf(d, bf16_to_f32(g.hst[o]), part[i][v]);
         } else {
           g.dxst[o] = f32_to_bf16(d);
         }
+      }
+    }
+  }
+  if (MODE == 0 && g.dgp != nullptr) {
+    // row sums over the tile's 256 columns: 32 lanes of a half-wave (fixed
+    // butterfly), then the 4 waves along N through LDS in wave order
+    float* red = reinterpret_cast<float*>(dsm);  // [DT_WN][DT_M]
+    __syncthreads();  // every wave is done with the stages
+#pragma unroll
+    for (int i = 0; i < DT_MBW; ++i) {
+      if (i >= mact) continue;  // uniform
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float t = part[i][v];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) t += __shfl_xor(t, off, 32);
+        if ((lane & 31) == 0)
+          red[wn * DT_M + wm * 32 * DT_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = t;
+      }
+    }
+    __syncthreads();
+    if (tid < rows) {
+      const int wmr = tid / (32 * DT_MBW), mb = (tid - wmr * 32 * DT_MBW) >> 5;
+      // rows of 32-row blocks past a wave's active count were never written
+      const int mrows_r = rows - wmr * 32 * DT_MBW;
+      if (mb < min(DT_MBW, (mrows_r + 31) >> 5)) {
+        const float t = ((red[tid] + red[DT_M + tid]) + red[2 * DT_M + tid]) + red[3 * DT_M + tid];
+        g.dgp[size_t(nt) * (g.TK + (g.n_exp - g.E) * g.T) + row_base + m0 + tid] = t;
       }
     }
   }
@@ -613,7 +673,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ 
 // Per token t: for each chosen expert k, the gate gradient dg = <dy_t, Y_k[t]>
 // (fixed-order block reduction) and the expert's output gradient g_k dy_t; the
 // shared expert's output gradient is dy_t itself.  dyst == nullptr: gate
-// gradients only.
+// gradients only; yst == nullptr: output gradients only.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dy,
                                                           const bf16_t* __restrict__ yst,
                                                           const int32_t* __restrict__ slot,
@@ -628,6 +688,23 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
   if (S > 0 && dyst != nullptr) {
     u32x4* o = reinterpret_cast<u32x4*>(dyst + size_t(TK + t) * H);
     for (int c = tid; c < nch; c += 256) o[c] = d8[c];
+  }
+  if (yst == nullptr) {  // output gradients only (the gate gradients come from dH)
+    for (int k = 0; k < K; ++k) {
+      const int sl = slot[t * K + k];
+      const float gk = gate[t * K + k];
+      u32x4* o = reinterpret_cast<u32x4*>(dyst + size_t(sl) * H);
+      for (int c = tid; c < nch; c += 256) {
+        const u32x4 dv = d8[c];
+        u32x4 ov;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ov[q] = uint32_t(f32_to_bf16(gk * __uint_as_float(dv[q] << 16))) |
+                  (uint32_t(f32_to_bf16(gk * __uint_as_float(dv[q] & 0xffff0000u))) << 16);
+        o[c] = ov;
+      }
+    }
+    return;
   }
   for (int k0 = 0; k0 < K; k0 += 32) {
     const int kn = min(32, K - k0);
@@ -677,15 +754,29 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
 // Per token: affinities of the chosen experts from the router partials (added
 // in partial order, as the selection does), gate normalisation and sigmoid
 // backward: ds_k = (dg_k - sum_j dg_j g_j) / S, dL_k = ds_k s_k (1 - s_k).
-// Writes dL per assignment [T][K] and per staged row.
+// Writes dL per assignment [T][K] and per staged row.  With dgp the gate
+// gradients are first formed from the data-gradient GEMM's row sums.
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ P, int ks,
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ slot,
-                                                         const float* __restrict__ dg, int T,
+                                                         float* __restrict__ dg, int T,
                                                          int E, int K, float* __restrict__ dl,
-                                                         float* __restrict__ dlst) {
+                                                         float* __restrict__ dlst,
+                                                         const float* __restrict__ dgp, int n_part,
+                                                         long long rows_total,
+                                                         const float* __restrict__ gate) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
+  if (dgp != nullptr) {
+    // dg_k = <dy, Y_k> = <dy W_down, H_k> = <dH_k, H_k> / g_k, dH_k = g_k dy W_down
+    // (the data-gradient GEMM's per-tile row sums, added in tile order)
+    for (int k = 0; k < K; ++k) {
+      const long long r = slot[t * K + k];
+      float a = 0.f;
+      for (int p = 0; p < n_part; ++p) a += dgp[p * rows_total + r];
+      dg[t * K + k] = a / gate[t * K + k];
+    }
+  }
   float s[32];
   float S = 0.f;
   for (int k = 0; k < K; ++k) {
@@ -836,13 +927,10 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
       hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned((size_t(rows) * I + 255) / 256)), dim3(256),
                          0, st, g.gst, g.ust, (long long)rows * I, g.hst);
       break;
-    case 2:  // combine backward
-      hipLaunchKernelGGL(combine_bwd_kernel, dim3(T), dim3(256), 0, st, dy, g.yst, slot, gate, T, K,
-                         H, g.TK, S, g.dyst, g.dg);
-      break;
-    case 3:  // router backward and the dgrad row-tile prefix
-      hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 255) / 256), dim3(256), 0, st, P, ks, idx,
-                         slot, g.dg, T, E, K, g.dl, g.dlst);
+    case 2:  // combine backward (without dgp; with dgp only the output gradients), tile prefixes
+      hipLaunchKernelGGL(combine_bwd_kernel, dim3(T), dim3(256), 0, st, dy,
+                         g.dgp != nullptr ? nullptr : g.yst, slot, gate, T, K, H, g.TK, S, g.dyst,
+                         g.dg);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       hipLaunchKernelGGL(bwd_tile_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T, BG_M,
                          const_cast<int32_t*>(g.mt));
@@ -851,6 +939,11 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
         hipLaunchKernelGGL(bwd_tile_prefix_kernel, dim3(1), dim3(64), 0, st, g.counts, E, S, T,
                            DT_M, g.mtd);
       }
+      break;
+    case 3:  // router backward (with dgp: after the dH GEMM)
+      hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 255) / 256), dim3(256), 0, st, P, ks, idx,
+                         slot, g.dg, T, E, K, g.dl, g.dlst, g.dgp, I / DG_N,
+                         (long long)(g.TK + S * T), gate);
       break;
     case 4:  // dH = dY W_down with the SwiGLU backward
       if (g.mtd != nullptr) return launch_dgrad_tile<0>(g, unsigned(dgrad_max_tiles(T, K, E, S) * (I / DT_N)), st);

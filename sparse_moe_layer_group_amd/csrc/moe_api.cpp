@@ -372,7 +372,7 @@ int run_experts_fp8(const moe_cfg& c, int T, const bf16_t* x, const moe_experts*
 // then the backward's staged rows and per-assignment buffers.
 struct BwdLayout {
   Layout f;
-  size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dl, dlst, wrt, dwrt, mt, mtd, total;
+  size_t xst, gst, ust, dyst, dgst, dust, dxst, dg, dgp, dl, dlst, wrt, dwrt, mt, mtd, total;
   // E4M3 weights
   size_t f32a, f32b, gq, gs, uq, us, dyq, dys, rowgate, dg32, du32, dgq, dgs, duq, dus;
   size_t kp, dyT, dysT, xT, xsT, hT, hsT, dgT, dgsT, duT, dusT;
@@ -438,6 +438,7 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
   B.dust = take(rows * I * 2);
   B.dxst = take(rows * H * 2);
   B.dg = take(TK * 4);
+  B.dgp = take((I / 256) * rows * 4);
   B.dl = take(TK * 4);
   B.dlst = take(TK * 4);
   B.wrt = take(E * H * 4);
@@ -525,6 +526,7 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   g.dust = at<bf16_t>(ws, B.dust);
   g.dxst = at<bf16_t>(ws, B.dxst);
   g.dg = at<float>(ws, B.dg);
+  g.dgp = at<float>(ws, B.dgp);  // gate gradients from dH and H: Y is not recomputed
   g.dl = at<float>(ws, B.dl);
   g.dlst = at<float>(ws, B.dlst);
   g.wrt = at<float>(ws, B.wrt);
@@ -545,28 +547,25 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   auto stage = [&](int s) {
     return moe::launch_backward_kernels(g, P, ks, r.idx, r.slot, r.gate, wr, dy, dx, dwr, st, s);
   };
-  // recompute the forward's expert intermediates from x (G, U, H and Y)
+  // recompute the forward's expert intermediates from x (G, U and H; Y is not
+  // needed: the gate gradients <dy, Y_k> = <dH_k, H_k> / g_k come out of the dH GEMM)
   MOE_TRY(timed(K_BWD_RECOMPUTE, st, [&]() -> hipError_t {
     hipError_t err = stage(0);
     if (err != hipSuccess) return err;
     if (run_plain_gemm(c, T, g.xst, g.w_gate, g.gst, I, H, r, ws, L, st) != MOE_OK ||
         run_plain_gemm(c, T, g.xst, g.w_up, g.ust, I, H, r, ws, L, st) != MOE_OK)
       return hipErrorLaunchFailure;
-    if ((err = stage(1)) != hipSuccess) return err;
-    if (run_plain_gemm(c, T, g.hst, g.w_down, g.yst, H, I, r, ws, L, st) != MOE_OK)
-      return hipErrorLaunchFailure;
-    return hipSuccess;
+    return stage(1);
   }));
-  MOE_TRY(timed(K_BWD_COMBINE, st, [&]() -> hipError_t {
-    hipError_t err = stage(2);
-    return err != hipSuccess ? err : stage(3);
-  }));
-  MOE_TRY(timed(K_BWD_DH, st, [&] { return stage(4); }));
+  MOE_TRY(timed(K_BWD_COMBINE, st, [&] { return stage(2); }));  // g dy, tile prefixes
+  MOE_TRY(timed(K_BWD_DH, st, [&] { return stage(4); }));       // dH, dG, dU, gate-gradient sums
   MOE_TRY(timed(K_BWD_DX, st, [&] { return stage(5); }));
   MOE_TRY(timed(K_BWD_WGRAD, st, [&] { return stage(6); }));
   MOE_TRY(timed(K_BWD_ROUTER, st, [&]() -> hipError_t {
-    hipError_t err = stage(7);
-    return err != hipSuccess ? err : stage(8);
+    hipError_t err = stage(3);
+    if (err != hipSuccess) return err;
+    if ((err = stage(7)) != hipSuccess) return err;
+    return stage(8);
   }));
   return MOE_OK;
 }
