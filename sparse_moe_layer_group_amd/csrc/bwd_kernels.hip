@@ -227,8 +227,9 @@ __global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
           const float G = bf16_to_f32(g.gst[o]), U = bf16_to_f32(g.ust[o]);
           const float sg = sigm(G);
           g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
-          g.dust[o] = f32_to_bf16(d * G * sg);
-          part[i][v] = fmaf(d, bf16_to_f32(g.hst[o]), part[i][v]);
+          const float du = d * G * sg;  // dH SiLU(G)
+          g.dust[o] = f32_to_bf16(du);
+          part[i][v] = fmaf(du, U, part[i][v]);  // dH H, H = SiLU(G) U
         } else {
           g.dxst[o] = f32_to_bf16(d);
         }
@@ -466,8 +467,9 @@ __global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
           const float G = bf16_to_f32(g.gst[o]), U = bf16_to_f32(g.ust[o]);
           const float sg = sigm(G);
           g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
-          g.dust[o] = f32_to_bf16(d * G * sg);
-          part[i][v] = fmaf(d, bf16_to_f32(g.hst[o]), part[i][v]);
+          const float du = d * G * sg;  // dH SiLU(G)
+          g.dust[o] = f32_to_bf16(du);
+          part[i][v] = fmaf(du, U, part[i][v]);  // dH H, H = SiLU(G) U
         } else {
           g.dxst[o] = f32_to_bf16(d);
         }
