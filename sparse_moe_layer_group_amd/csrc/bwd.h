@@ -37,7 +37,8 @@ struct BwdArgs {
   float* dw_up;               // [E+S][I][H] float32 out
   float* dw_down;             // [E+S][H][I] float32 out
   int E, n_exp, T, TK, K, H, I;
-  int wg_xcd;                 // weight-gradient tiles in XCD-contiguous order
+  int wg_xcd;                 // decode-sized batch (at most 64 rows per routed expert): the
+                              // per-tile weight-gradient kernel, else the persistent one
 };
 
 int bwd_max_row_tiles(int T, int K, int E, int S);

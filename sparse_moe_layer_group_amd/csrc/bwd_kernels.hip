@@ -21,7 +21,10 @@
 //     batches): 128 x 256 tiles, four waves, K steps of 32 in three stages;
 //   - wgrad:  out[m][n] = sum over the expert's rows r of A[r][m] B[r][n]
 //     (dW_down = dY^T H, dW_gate = dG^T X, dW_up = dU^T X), float32 out;
-//     128 x 256 tiles, four waves, K steps of 32 rows in three stages.
+//     128 x 256 tiles, K steps of 32 rows.  wgrad_ws_kernel (more than 64
+//     rows per routed expert): one persistent workgroup per CU, four copy and
+//     four MFMA waves, six stages; wgrad_gemm_kernel (decode-sized batches):
+//     one workgroup of four waves per tile, three stages.
 // Operands whose contraction index is their slow (row) dimension are staged in
 // LDS as "k-rows" in memory order and read with ds_read_b64_tr_b16: in each
 // group of 16 lanes, source lane s addresses 4 consecutive columns of k-row
@@ -507,6 +510,9 @@ __global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
 }
 
 // ---------------------------------------------------------------- wgrad GEMM
+// (one workgroup per tile, for decode-sized batches of up to 64 rows per
+// routed expert, where the tiles are nearly pure stores; wgrad_ws_kernel below
+// serves larger batches.)
 // out[e][m][n] = sum over expert e's rows r of A[r][m] B[r][n], float32.
 // MODE 0: dW_down (A = dY [.][hidden], B = H [.][inter]);
 // MODE 1: dW_gate (A = dG [.][inter], B = X [.][hidden]); MODE 2: dW_up (A = dU).
@@ -530,18 +536,16 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
   const int N = MODE == 0 ? g.I : g.H;
   const int tm = M / BG_M, tn = N / WG_N;
   // experts in reverse order: the shared experts' tiles, which contract over
-  // all T rows, start first instead of forming the launch's tail
-  // With g.wg_xcd (decode-sized batches, set by the host): workgroup b runs
-  // on XCD b % 8; the shared experts' tiles are dealt round-robin and the
-  // routed experts' tiles to the XCDs in contiguous eighths, so each XCD
-  // writes a contiguous eighth of the gradients (at 256 tokens, where these
-  // tiles are nearly pure stores: 7.9 -> 7.3 ms for the three launches; at
-  // 8192 tokens it measured 1% slower).  The shared tiles' count is a multiple
-  // of 8, and the launch holds 8 ceil(routed tiles / 8) slots past them.
+  // all T rows, start first instead of forming the launch's tail.  Workgroup
+  // b runs on XCD b % 8; the shared experts' tiles are dealt round-robin and
+  // the routed experts' tiles to the XCDs in contiguous eighths, so each XCD
+  // writes a contiguous eighth of the gradients (7.9 -> 7.3 ms for the three
+  // launches at 256 tokens).  The shared tiles' count is a multiple of 8, and
+  // the launch holds 8 ceil(routed tiles / 8) slots past them.
   const int per_e = tm * tn;
   const int sh_tiles = (g.n_exp - g.E) * per_e;
   int task = blockIdx.x;
-  if (g.wg_xcd && task >= sh_tiles) {
+  if (task >= sh_tiles) {
     const int b = task - sh_tiles, rt = g.E * per_e, per = (rt + 7) >> 3;
     const int j = b >> 3;
     task = sh_tiles + (b & 7) * per + j;
@@ -646,6 +650,207 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
     }
   // (staging the tile through LDS for 1 KB row stores measured no better here:
   // +0.9% at 8192 tokens, -3% at 256)
+}
+
+// ---------------------------------------------------------------- wgrad, persistent
+// The products of wgrad_gemm_kernel with its waves split by role, so that the
+// gradient stores overlap the copies and MFMAs of the tiles after them.  One
+// workgroup per CU walks a fixed list of 128 x 256 tiles: the shared experts'
+// tiles dealt round-robin over all workgroups, then routed expert e's tiles
+// dealt round-robin over the workgroups with b % 8 == e % 8 (workgroup b runs
+// on XCD b % 8, so each expert's operands are fetched into one L2).
+//   - waves 4-7 only copy: k-steps of 32 rows into a ring of WS_NS LDS stages,
+//     WS_NS - 1 steps ahead; before barrier p they wait until steps p and p + 1
+//     have landed, after it they refill the stage step p - 1 used;
+//   - waves 0-3 only compute (64 x 128 each, as wgrad_gemm_kernel's waves) and
+//     store.  Such a wave never waits for a load issued after its stores, so
+//     the stores drain while the next tiles run.  Each step's first k16 slice
+//     is read in the step before (barrier p certifies step p + 1).
+// Stores keep the MFMA's layout: 4-byte stores, 32 lanes on 128 contiguous
+// bytes of one gradient row.  (16-byte stores measured slower: after 4 x 4
+// transposes within lane quads, 8 rows x 128 bytes per instruction, +13% at
+// 8192 tokens; with the operands swapped, 32 rows x 32 bytes, 2-4x.)
+namespace {
+constexpr int WS_NS = 6;                                // LDS stages
+constexpr int WS_NT = 512;                              // 4 compute + 4 copy waves
+constexpr int WS_CPW = WG_ACP + WG_BCP;                 // copies per copy wave and step (6)
+static_assert(WS_CPW * (WS_NS - 2) < 64, "vmcnt holds 6 bits");
+
+struct WsTile {
+  int e, m0, n0, base, cnt;
+};
+
+// Tile i of workgroup b's list (G workgroups), or false past its end; the
+// experts' (first row, rows) from the LDS copies rb, rc
+MOE_DEV bool ws_tile(const BwdArgs& g, const int* rb, const int* rc, int tm, int tn, int b, int G, int i,
+                     WsTile& t) {
+  const int per_e = tm * tn;
+  const int sh = (g.n_exp - g.E) * per_e;
+  const int n_sh = b < sh ? (sh - 1 - b) / G + 1 : 0;
+  int e, q;
+  if (i < n_sh) {
+    const int task = b + i * G;
+    e = g.E + task / per_e;
+    q = task - (e - g.E) * per_e;
+  } else {
+    const int x = b & 7, nx = (G - 1 - x) / 8 + 1;  // workgroups on XCD x
+    const int task = (b >> 3) + (i - n_sh) * nx;
+    const int eo = task / per_e;
+    e = x + 8 * eo;
+    if (e >= g.E) return false;
+    q = task - eo * per_e;
+  }
+  // row-major over the expert's tiles: the XCD's workgroups write whole rows
+  // of the gradient at a time (column-major, which fetches 2.5x fewer operand
+  // bytes for dW_gate and dW_up, measured 27% slower at 8192 tokens)
+  const int mt = q / tn, nt = q - mt * tn;
+  t.e = e;
+  t.m0 = mt * BG_M;
+  t.n0 = nt * WG_N;
+  t.base = rb[e];
+  t.cnt = rc[e];
+  return true;
+}
+}  // namespace
+
+template <int MODE>
+__global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
+  // WS_NS stages of WG_STAGE, then every expert's first row and rows: read
+  // from LDS, the tile walk issues no global load (a wave that has stores in
+  // flight would wait for them before one)
+  extern __shared__ __attribute__((aligned(16))) bf16_t wsm[];
+  int* rb = reinterpret_cast<int*>(wsm + WS_NS * WG_STAGE);
+  int* rc = rb + g.n_exp;
+  const int M = MODE == 0 ? g.H : g.I;
+  const int N = MODE == 0 ? g.I : g.H;
+  const int tm = M / BG_M, tn = N / WG_N;
+  const int b = blockIdx.x, G = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int e = tid; e < g.n_exp; e += WS_NT) expert_rows(g, e, rb[e], rc[e]);
+  __syncthreads();
+  WsTile t;
+
+  if (wave >= 4) {
+    // ---- copy waves.  Copy wave c: A copies 2c, 2c + 1 (k-rows 4 (2c + i) .. +3,
+    // lane l: + l/16, position l%16), B copies 4c .. 4c + 3 (k-rows 2 (4c + i) .. +1)
+    const int c = wave - 4;
+    const uint32_t total_rows = uint32_t(g.TK + (g.n_exp - g.E) * g.T);
+    const bf16_t* ap = MODE == 0 ? g.dyst : (MODE == 1 ? g.dgst : g.dust);
+    const bf16_t* bp = MODE == 0 ? g.hst : g.xst;
+    const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(ap, total_rows * uint32_t(M) * 2u);
+    const __amdgpu_buffer_rsrc_t br = buffer_rsrc(bp, total_rows * uint32_t(N) * 2u);
+    int akr[WG_ACP], ach[WG_ACP], bkr[WG_BCP], bch[WG_BCP];
+#pragma unroll
+    for (int i = 0; i < WG_ACP; ++i) {
+      akr[i] = 4 * (WG_ACP * c + i) + (lane >> 4);
+      ach[i] = kswz(akr[i], lane & 15) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < WG_BCP; ++i) {
+      bkr[i] = 2 * (WG_BCP * c + i) + (lane >> 5);
+      bch[i] = kswz(bkr[i], lane & 31) * 8;
+    }
+    // look-ahead cursor: step lk of tile li (tiles without rows have no steps)
+    int li = 0, lk = 0, issued = 0;
+    WsTile lt;
+    bool more = ws_tile(g, rb, rc, tm, tn, b, G, 0, lt);
+    while (more && lt.cnt == 0) more = ws_tile(g, rb, rc, tm, tn, b, G, ++li, lt);
+    auto issue = [&]() {
+      bf16_t* st = wsm + (issued % WS_NS) * WG_STAGE;
+      const int r0 = lk * BG_K;
+#pragma unroll
+      for (int i = 0; i < WG_ACP; ++i) {
+        const int r = r0 + akr[i];
+        const uint32_t o =
+            r < lt.cnt ? (uint32_t(lt.base + r) * uint32_t(M) + uint32_t(lt.m0 + ach[i])) * 2u : 0xfffffff0u;
+        copy16_to_lds(ar, o, st + 4 * (WG_ACP * c + i) * BG_M);
+      }
+#pragma unroll
+      for (int i = 0; i < WG_BCP; ++i) {
+        const int r = r0 + bkr[i];
+        const uint32_t o =
+            r < lt.cnt ? (uint32_t(lt.base + r) * uint32_t(N) + uint32_t(lt.n0 + bch[i])) * 2u : 0xfffffff0u;
+        copy16_to_lds(br, o, st + BG_K * BG_M + 2 * (WG_BCP * c + i) * WG_N);
+      }
+      ++issued;
+      if (++lk * BG_K >= lt.cnt) {
+        lk = 0;
+        do more = ws_tile(g, rb, rc, tm, tn, b, G, ++li, lt);
+        while (more && lt.cnt == 0);
+      }
+    };
+    for (int s = 0; s < WS_NS - 1 && more; ++s) issue();
+    if (issued == WS_NS - 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(WS_CPW * (WS_NS - 2)));
+    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    __builtin_amdgcn_s_barrier();  // step 0 landed
+    int p = 0;
+    for (int i = 0; ws_tile(g, rb, rc, tm, tn, b, G, i, t); ++i) {
+      const int nk = (t.cnt + BG_K - 1) / BG_K;
+      for (int kt = 0; kt < nk; ++kt, ++p) {
+        // steps p and p + 1 landed: the copies of p + 2 .. issued - 1 may still fly
+        if (issued - p - 2 == WS_NS - 3) __builtin_amdgcn_s_waitcnt(vm_wait_imm(WS_CPW * (WS_NS - 3)));
+        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (more) issue();  // step p + WS_NS - 1 into the stage of step p - 1
+      }
+    }
+    return;
+  }
+
+  // ---- compute waves
+  const int wm = wave >> 1, wn = wave & 1;
+  float* outb = MODE == 0 ? g.dw_down : (MODE == 1 ? g.dw_gate : g.dw_up);
+  auto frags = [&](const bf16_t* st, int s, bf16x8* af, bf16x8* bf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) af[i] = tr_frag<BG_M>(st, 16 * s, wm * 64 + 32 * i, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = tr_frag<WG_N>(st + BG_K * BG_M, 16 * s, wn * 128 + 32 * j, lane);
+  };
+  __builtin_amdgcn_s_barrier();  // step 0 landed
+  asm volatile("" ::: "memory");
+  bf16x8 a0[2], b0[4];  // the first k16 slice of the coming step
+  frags(wsm, 0, a0, b0);
+  int p = 0;
+  for (int i = 0; ws_tile(g, rb, rc, tm, tn, b, G, i, t); ++i) {
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[u][j][v] = 0.f;
+    const int nk = (t.cnt + BG_K - 1) / BG_K;
+    for (int kt = 0; kt < nk; ++kt, ++p) {
+      __builtin_amdgcn_s_barrier();  // steps p and p + 1 landed; step p - 1's stage is being refilled
+      asm volatile("" ::: "memory");
+      const bf16_t* st = wsm + (p % WS_NS) * WG_STAGE;
+      bf16x8 a1[2], b1[4];
+      frags(st, 1, a1, b1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[u], b0[j], acc[u][j], 0, 0, 0);
+      frags(wsm + ((p + 1) % WS_NS) * WG_STAGE, 0, a0, b0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[u], b1[j], acc[u][j], 0, 0, 0);
+    }
+    // lane l holds column n0 + wn 128 + 32 j + l%32 of rows m0 + wm 64 + 32 u + 8 (v/4) + 4 (l/32) + v%4
+    float* out = outb + size_t(t.e) * M * N + size_t(t.m0 + wm * 64 + 4 * (lane >> 5)) * N + t.n0 + wn * 128 +
+                 (lane & 31);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)  // written once, never read here: non-temporal
+          __builtin_nontemporal_store(acc[u][j][v], out + size_t(32 * u + 8 * (v >> 2) + (v & 3)) * N + 32 * j);
+  }
 }
 
 // ---------------------------------------------------------------- row kernels
@@ -912,6 +1117,27 @@ hipError_t launch_dgrad_tile(const BwdArgs& g, unsigned blocks, hipStream_t st) 
   hipLaunchKernelGGL(dgrad_tile_kernel<MODE>, dim3(blocks), dim3(DT_NT), lds, st, g);
   return hipGetLastError();
 }
+
+// One persistent workgroup per CU (at least 8, one per XCD)
+template <int MODE>
+hipError_t launch_wgrad_ws(const BwdArgs& g, hipStream_t st) {
+  constexpr int kLdsMax = 160 * 1024;  // LDS per CU
+  static bool attr_set = false;
+  const size_t lds = size_t(WS_NS) * WG_STAGE * sizeof(bf16_t) + 2 * sizeof(int) * size_t(g.n_exp);
+  if (lds > size_t(kLdsMax)) return hipErrorInvalidValue;  // over 2000 experts
+  if (!attr_set) {
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_ws_kernel<MODE>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(wgrad_ws_kernel<MODE>, dim3(unsigned(cus < 8 ? 8 : cus)), dim3(WS_NT), lds, st, g);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, const int32_t* idx,
@@ -958,6 +1184,12 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
                          dim3(BG_NT), 0, st, g);
       break;
     case 6: {  // weight gradients
+      if (!g.wg_xcd) {  // more than 64 rows per routed expert on average: persistent
+        hipError_t err = launch_wgrad_ws<0>(g, st);
+        if (err == hipSuccess) err = launch_wgrad_ws<1>(g, st);
+        if (err == hipSuccess) err = launch_wgrad_ws<2>(g, st);
+        return err;
+      }
       const unsigned per_e = unsigned((H / BG_M) * (I / WG_N));
       const unsigned tiles = per_e * S + 8 * ((per_e * E + 7) / 8);  // slots past the tiles exit
       hipLaunchKernelGGL(wgrad_gemm_kernel<0>, dim3(tiles), dim3(BG_NT), 0, st, g);

@@ -68,8 +68,11 @@ def _row_rel(a, b):
 # mid T=3000: 293-454 rows per expert (two 320-row data-gradient tiles for some,
 # weight-gradient K loops with ragged tails); T=300: the large-tile data-gradient
 # kernel with one tile; T=65 and 1: the 128-row kernel
+# mid T=3000 and mid_skew T=800 take the persistent weight-gradient kernel (more
+# than 64 rows per routed expert); mid_skew T=800 has two experts without rows
+# (all-zero gradient tiles) and one with 792 rows (25 k-steps)
 @pytest.mark.parametrize("name,T", [("mid", 300), ("mid", 65), ("mid", 1), ("mid_skew", 300),
-                                    ("mid", 3000)])
+                                    ("mid", 3000), ("mid_skew", 800)])
 def test_backward_parity(name, T):
     c = S.get_config(name, T=T)
     say(f"backward parity: {name} T={T}")
