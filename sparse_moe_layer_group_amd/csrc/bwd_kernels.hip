@@ -659,6 +659,7 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
 // tiles dealt round-robin over all workgroups, then routed expert e's tiles
 // dealt round-robin over the workgroups with b % 8 == e % 8 (workgroup b runs
 // on XCD b % 8, so each expert's operands are fetched into one L2).
+// MODE 0: dW_down; MODE 1: dW_gate and dW_up, each tile's two in a row.
 //   - waves 4-7 only copy: k-steps of 32 rows into a ring of WS_NS LDS stages,
 //     WS_NS - 1 steps ahead; before barrier p they wait until steps p and p + 1
 //     have landed, after it they refill the stage step p - 1 used;
@@ -677,14 +678,16 @@ constexpr int WS_CPW = WG_ACP + WG_BCP;                 // copies per copy wave 
 static_assert(WS_CPW * (WS_NS - 2) < 64, "vmcnt holds 6 bits");
 
 struct WsTile {
-  int e, m0, n0, base, cnt;
+  int e, m0, n0, base, cnt, mode;
 };
 
 // Tile i of workgroup b's list (G workgroups), or false past its end; the
-// experts' (first row, rows) from the LDS copies rb, rc
-MOE_DEV bool ws_tile(const BwdArgs& g, const int* rb, const int* rc, int tm, int tn, int b, int G, int i,
-                     WsTile& t) {
-  const int per_e = tm * tn;
+// experts' (first row, rows) from the LDS copies rb, rc.  With nmode = 2
+// (dW_gate and dW_up in one launch) each tile comes twice in a row, mode 0
+// then 1: the two share their X slab, which is then fetched once.
+MOE_DEV bool ws_tile(const BwdArgs& g, const int* rb, const int* rc, int tm, int tn, int nmode, int b, int G,
+                     int i, WsTile& t) {
+  const int per_e = tm * tn * nmode;
   const int sh = (g.n_exp - g.E) * per_e;
   const int n_sh = b < sh ? (sh - 1 - b) / G + 1 : 0;
   int e, q;
@@ -703,6 +706,8 @@ MOE_DEV bool ws_tile(const BwdArgs& g, const int* rb, const int* rc, int tm, int
   // row-major over the expert's tiles: the XCD's workgroups write whole rows
   // of the gradient at a time (column-major, which fetches 2.5x fewer operand
   // bytes for dW_gate and dW_up, measured 27% slower at 8192 tokens)
+  t.mode = nmode == 2 ? (q & 1) : 0;
+  if (nmode == 2) q >>= 1;
   const int mt = q / tn, nt = q - mt * tn;
   t.e = e;
   t.m0 = mt * BG_M;
@@ -721,6 +726,7 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
   extern __shared__ __attribute__((aligned(16))) bf16_t wsm[];
   int* rb = reinterpret_cast<int*>(wsm + WS_NS * WG_STAGE);
   int* rc = rb + g.n_exp;
+  constexpr int NMODE = MODE == 0 ? 1 : 2;
   const int M = MODE == 0 ? g.H : g.I;
   const int N = MODE == 0 ? g.I : g.H;
   const int tm = M / BG_M, tn = N / WG_N;
@@ -736,10 +742,9 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
     // lane l: + l/16, position l%16), B copies 4c .. 4c + 3 (k-rows 2 (4c + i) .. +1)
     const int c = wave - 4;
     const uint32_t total_rows = uint32_t(g.TK + (g.n_exp - g.E) * g.T);
-    const bf16_t* ap = MODE == 0 ? g.dyst : (MODE == 1 ? g.dgst : g.dust);
-    const bf16_t* bp = MODE == 0 ? g.hst : g.xst;
-    const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(ap, total_rows * uint32_t(M) * 2u);
-    const __amdgpu_buffer_rsrc_t br = buffer_rsrc(bp, total_rows * uint32_t(N) * 2u);
+    const __amdgpu_buffer_rsrc_t ar0 = buffer_rsrc(MODE == 0 ? g.dyst : g.dgst, total_rows * uint32_t(M) * 2u);
+    const __amdgpu_buffer_rsrc_t ar1 = buffer_rsrc(MODE == 0 ? g.dyst : g.dust, total_rows * uint32_t(M) * 2u);
+    const __amdgpu_buffer_rsrc_t br = buffer_rsrc(MODE == 0 ? g.hst : g.xst, total_rows * uint32_t(N) * 2u);
     int akr[WG_ACP], ach[WG_ACP], bkr[WG_BCP], bch[WG_BCP];
 #pragma unroll
     for (int i = 0; i < WG_ACP; ++i) {
@@ -754,11 +759,12 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
     // look-ahead cursor: step lk of tile li (tiles without rows have no steps)
     int li = 0, lk = 0, issued = 0;
     WsTile lt;
-    bool more = ws_tile(g, rb, rc, tm, tn, b, G, 0, lt);
-    while (more && lt.cnt == 0) more = ws_tile(g, rb, rc, tm, tn, b, G, ++li, lt);
+    bool more = ws_tile(g, rb, rc, tm, tn, NMODE, b, G, 0, lt);
+    while (more && lt.cnt == 0) more = ws_tile(g, rb, rc, tm, tn, NMODE, b, G, ++li, lt);
     auto issue = [&]() {
       bf16_t* st = wsm + (issued % WS_NS) * WG_STAGE;
       const int r0 = lk * BG_K;
+      const __amdgpu_buffer_rsrc_t ar = lt.mode ? ar1 : ar0;
 #pragma unroll
       for (int i = 0; i < WG_ACP; ++i) {
         const int r = r0 + akr[i];
@@ -776,7 +782,7 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
       ++issued;
       if (++lk * BG_K >= lt.cnt) {
         lk = 0;
-        do more = ws_tile(g, rb, rc, tm, tn, b, G, ++li, lt);
+        do more = ws_tile(g, rb, rc, tm, tn, NMODE, b, G, ++li, lt);
         while (more && lt.cnt == 0);
       }
     };
@@ -785,7 +791,7 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
     else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     __builtin_amdgcn_s_barrier();  // step 0 landed
     int p = 0;
-    for (int i = 0; ws_tile(g, rb, rc, tm, tn, b, G, i, t); ++i) {
+    for (int i = 0; ws_tile(g, rb, rc, tm, tn, NMODE, b, G, i, t); ++i) {
       const int nk = (t.cnt + BG_K - 1) / BG_K;
       for (int kt = 0; kt < nk; ++kt, ++p) {
         // steps p and p + 1 landed: the copies of p + 2 .. issued - 1 may still fly
@@ -801,7 +807,6 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
 
   // ---- compute waves
   const int wm = wave >> 1, wn = wave & 1;
-  float* outb = MODE == 0 ? g.dw_down : (MODE == 1 ? g.dw_gate : g.dw_up);
   auto frags = [&](const bf16_t* st, int s, bf16x8* af, bf16x8* bf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) af[i] = tr_frag<BG_M>(st, 16 * s, wm * 64 + 32 * i, lane);
@@ -813,7 +818,7 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
   bf16x8 a0[2], b0[4];  // the first k16 slice of the coming step
   frags(wsm, 0, a0, b0);
   int p = 0;
-  for (int i = 0; ws_tile(g, rb, rc, tm, tn, b, G, i, t); ++i) {
+  for (int i = 0; ws_tile(g, rb, rc, tm, tn, NMODE, b, G, i, t); ++i) {
     f32x16 acc[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -841,6 +846,7 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
           acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[u], b1[j], acc[u][j], 0, 0, 0);
     }
     // lane l holds column n0 + wn 128 + 32 j + l%32 of rows m0 + wm 64 + 32 u + 8 (v/4) + 4 (l/32) + v%4
+    float* outb = MODE == 0 ? g.dw_down : (t.mode ? g.dw_up : g.dw_gate);
     float* out = outb + size_t(t.e) * M * N + size_t(t.m0 + wm * 64 + 4 * (lane >> 5)) * N + t.n0 + wn * 128 +
                  (lane & 31);
 #pragma unroll
@@ -1186,8 +1192,7 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
     case 6: {  // weight gradients
       if (!g.wg_xcd) {  // more than 64 rows per routed expert on average: persistent
         hipError_t err = launch_wgrad_ws<0>(g, st);
-        if (err == hipSuccess) err = launch_wgrad_ws<1>(g, st);
-        if (err == hipSuccess) err = launch_wgrad_ws<2>(g, st);
+        if (err == hipSuccess) err = launch_wgrad_ws<1>(g, st);  // dW_gate and dW_up
         return err;
       }
       const unsigned per_e = unsigned((H / BG_M) * (I / WG_N));
