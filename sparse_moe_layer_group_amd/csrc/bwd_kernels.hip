@@ -672,10 +672,19 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
 // transposes within lane quads, 8 rows x 128 bytes per instruction, +13% at
 // 8192 tokens; with the operands swapped, 32 rows x 32 bytes, 2-4x.)
 namespace {
+// Measured at 8192 tokens against this shape (12.65 ms for the stage): barrier
+// p certifying step p only, 12.86 ms; two workgroups per CU of four MFMA and
+// two copy waves with three stages each, 14.59 ms.
 constexpr int WS_NS = 6;                                // LDS stages
-constexpr int WS_NT = 512;                              // 4 compute + 4 copy waves
-constexpr int WS_CPW = WG_ACP + WG_BCP;                 // copies per copy wave and step (6)
+constexpr int WS_CW = 4;                                // copy waves
+constexpr int WS_PF = 1;                                // barrier p certifies steps p and p + 1
+constexpr int WS_BPC = 1;                               // workgroups per CU
+constexpr int WS_NT = 64 * (4 + WS_CW);                 // 4 compute waves + the copy waves
+constexpr int WS_ACP = BG_K * BG_M * 2 / 1024 / WS_CW;  // 1 KB A copies per copy wave and step
+constexpr int WS_BCP = BG_K * WG_N * 2 / 1024 / WS_CW;  // ... B copies
+constexpr int WS_CPW = WS_ACP + WS_BCP;                 // copies per copy wave and step
 static_assert(WS_CPW * (WS_NS - 2) < 64, "vmcnt holds 6 bits");
+static_assert(WS_NS >= 3 + WS_PF, "a stage is refilled only after its step was read");
 
 struct WsTile {
   int e, m0, n0, base, cnt, mode;
@@ -719,7 +728,8 @@ MOE_DEV bool ws_tile(const BwdArgs& g, const int* rb, const int* rc, int tm, int
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
+// (the second bound is waves per SIMD: WS_BPC workgroups of 4 + WS_CW waves per CU)
+__global__ __launch_bounds__(WS_NT, WS_BPC * (4 + WS_CW) / 4) void wgrad_ws_kernel(BwdArgs g) {
   // WS_NS stages of WG_STAGE, then every expert's first row and rows: read
   // from LDS, the tile walk issues no global load (a wave that has stores in
   // flight would wait for them before one)
@@ -745,15 +755,15 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
     const __amdgpu_buffer_rsrc_t ar0 = buffer_rsrc(MODE == 0 ? g.dyst : g.dgst, total_rows * uint32_t(M) * 2u);
     const __amdgpu_buffer_rsrc_t ar1 = buffer_rsrc(MODE == 0 ? g.dyst : g.dust, total_rows * uint32_t(M) * 2u);
     const __amdgpu_buffer_rsrc_t br = buffer_rsrc(MODE == 0 ? g.hst : g.xst, total_rows * uint32_t(N) * 2u);
-    int akr[WG_ACP], ach[WG_ACP], bkr[WG_BCP], bch[WG_BCP];
+    int akr[WS_ACP], ach[WS_ACP], bkr[WS_BCP], bch[WS_BCP];
 #pragma unroll
-    for (int i = 0; i < WG_ACP; ++i) {
-      akr[i] = 4 * (WG_ACP * c + i) + (lane >> 4);
+    for (int i = 0; i < WS_ACP; ++i) {
+      akr[i] = 4 * (WS_ACP * c + i) + (lane >> 4);
       ach[i] = kswz(akr[i], lane & 15) * 8;
     }
 #pragma unroll
-    for (int i = 0; i < WG_BCP; ++i) {
-      bkr[i] = 2 * (WG_BCP * c + i) + (lane >> 5);
+    for (int i = 0; i < WS_BCP; ++i) {
+      bkr[i] = 2 * (WS_BCP * c + i) + (lane >> 5);
       bch[i] = kswz(bkr[i], lane & 31) * 8;
     }
     // look-ahead cursor: step lk of tile li (tiles without rows have no steps)
@@ -766,18 +776,18 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
       const int r0 = lk * BG_K;
       const __amdgpu_buffer_rsrc_t ar = lt.mode ? ar1 : ar0;
 #pragma unroll
-      for (int i = 0; i < WG_ACP; ++i) {
+      for (int i = 0; i < WS_ACP; ++i) {
         const int r = r0 + akr[i];
         const uint32_t o =
             r < lt.cnt ? (uint32_t(lt.base + r) * uint32_t(M) + uint32_t(lt.m0 + ach[i])) * 2u : 0xfffffff0u;
-        copy16_to_lds(ar, o, st + 4 * (WG_ACP * c + i) * BG_M);
+        copy16_to_lds(ar, o, st + 4 * (WS_ACP * c + i) * BG_M);
       }
 #pragma unroll
-      for (int i = 0; i < WG_BCP; ++i) {
+      for (int i = 0; i < WS_BCP; ++i) {
         const int r = r0 + bkr[i];
         const uint32_t o =
             r < lt.cnt ? (uint32_t(lt.base + r) * uint32_t(N) + uint32_t(lt.n0 + bch[i])) * 2u : 0xfffffff0u;
-        copy16_to_lds(br, o, st + BG_K * BG_M + 2 * (WG_BCP * c + i) * WG_N);
+        copy16_to_lds(br, o, st + BG_K * BG_M + 2 * (WS_BCP * c + i) * WG_N);
       }
       ++issued;
       if (++lk * BG_K >= lt.cnt) {
@@ -787,15 +797,19 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
       }
     };
     for (int s = 0; s < WS_NS - 1 && more; ++s) issue();
-    if (issued == WS_NS - 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(WS_CPW * (WS_NS - 2)));
-    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-    __builtin_amdgcn_s_barrier();  // step 0 landed
+    if (WS_PF) {
+      if (issued == WS_NS - 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(WS_CPW * (WS_NS - 2)));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+      __builtin_amdgcn_s_barrier();  // step 0 landed
+    }
     int p = 0;
     for (int i = 0; ws_tile(g, rb, rc, tm, tn, NMODE, b, G, i, t); ++i) {
       const int nk = (t.cnt + BG_K - 1) / BG_K;
       for (int kt = 0; kt < nk; ++kt, ++p) {
-        // steps p and p + 1 landed: the copies of p + 2 .. issued - 1 may still fly
-        if (issued - p - 2 == WS_NS - 3) __builtin_amdgcn_s_waitcnt(vm_wait_imm(WS_CPW * (WS_NS - 3)));
+        // steps p (and with WS_PF p + 1) landed: the copies of p + 1 + WS_PF ..
+        // issued - 1 may still fly
+        if (issued - p - 1 - WS_PF == WS_NS - 2 - WS_PF)
+          __builtin_amdgcn_s_waitcnt(vm_wait_imm(WS_CPW * (WS_NS - 2 - WS_PF)));
         else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -813,10 +827,12 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = tr_frag<WG_N>(st + BG_K * BG_M, 16 * s, wn * 128 + 32 * j, lane);
   };
-  __builtin_amdgcn_s_barrier();  // step 0 landed
-  asm volatile("" ::: "memory");
   bf16x8 a0[2], b0[4];  // the first k16 slice of the coming step
-  frags(wsm, 0, a0, b0);
+  if (WS_PF) {
+    __builtin_amdgcn_s_barrier();  // step 0 landed
+    asm volatile("" ::: "memory");
+    frags(wsm, 0, a0, b0);
+  }
   int p = 0;
   for (int i = 0; ws_tile(g, rb, rc, tm, tn, NMODE, b, G, i, t); ++i) {
     f32x16 acc[2][4];
@@ -832,13 +848,14 @@ __global__ __launch_bounds__(WS_NT, 1) void wgrad_ws_kernel(BwdArgs g) {
       asm volatile("" ::: "memory");
       const bf16_t* st = wsm + (p % WS_NS) * WG_STAGE;
       bf16x8 a1[2], b1[4];
+      if (!WS_PF) frags(st, 0, a0, b0);
       frags(st, 1, a1, b1);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[u], b0[j], acc[u][j], 0, 0, 0);
-      frags(wsm + ((p + 1) % WS_NS) * WG_STAGE, 0, a0, b0);
+      if (WS_PF) frags(wsm + ((p + 1) % WS_NS) * WG_STAGE, 0, a0, b0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -1130,7 +1147,7 @@ hipError_t launch_wgrad_ws(const BwdArgs& g, hipStream_t st) {
   constexpr int kLdsMax = 160 * 1024;  // LDS per CU
   static bool attr_set = false;
   const size_t lds = size_t(WS_NS) * WG_STAGE * sizeof(bf16_t) + 2 * sizeof(int) * size_t(g.n_exp);
-  if (lds > size_t(kLdsMax)) return hipErrorInvalidValue;  // over 2000 experts
+  if (lds * WS_BPC > size_t(kLdsMax)) return hipErrorInvalidValue;  // too many experts
   if (!attr_set) {
     const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_ws_kernel<MODE>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
@@ -1141,7 +1158,7 @@ hipError_t launch_wgrad_ws(const BwdArgs& g, hipStream_t st) {
   hipError_t err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(wgrad_ws_kernel<MODE>, dim3(unsigned(cus < 8 ? 8 : cus)), dim3(WS_NT), lds, st, g);
+  hipLaunchKernelGGL(wgrad_ws_kernel<MODE>, dim3(unsigned(WS_BPC * (cus < 8 ? 8 : cus))), dim3(WS_NT), lds, st, g);
   return hipGetLastError();
 }
 }  // namespace
