@@ -60,7 +60,7 @@ KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
                   "prefill": _COMMON_SOURCES + ("tile_gemm.hip",),
                   "skew": _COMMON_SOURCES + ("stream_gemm.hip", "tile_gemm.hip"),
                   "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",),
-                  # backward: the weight-gradient stage (three launches per call)
+                  # backward: the weight-gradient stage (all its launches in one call)
                   "backward_prefill_bf16": _COMMON_SOURCES + ("bwd.h", "bwd_kernels.hip"),
                   "backward_prefill_e4m3": _COMMON_SOURCES + ("bwd.h", "bwd_fp8_kernels.hip")}
 
@@ -79,7 +79,7 @@ def kernel_sources_sha256(workload):
 
 def measured_traffic(workload):
     """HBM bytes per launch of the roofline's kernel (gemm_gate_up; the backward's
-    three weight-gradient launches together), or None when not measured for the
+    weight-gradient launches of one call together), or None when not measured for the
     current sources."""
     t = MEASURED_TRAFFIC.get(workload)
     if not t or not COPY_CALIBRATION or t["src_sha256"] != kernel_sources_sha256(workload):
@@ -399,18 +399,17 @@ def bench_backward(args, np, torch, moe, S):
 
     rows = T * K + Sn * T
     mfma_peak = MFMA_PEAK_TFLOPS["e4m3" if f8 else "bf16"]
-    # weight-gradient GEMMs (one call = three launches: dW_down, dW_gate, dW_up):
-    # float32 gradients of every expert written once, staged operands read once
-    # per launch (dY and H; dG and X; dU and X), wb bytes per element (E4M3:
-    # their 128x1 codes)
+    # weight-gradient GEMMs (dW_down, dW_gate, dW_up; two or three launches a
+    # call): float32 gradients of every expert written once, each staged operand
+    # read once (dY, H, dG, dU, X), wb bytes per element (E4M3: their 128x1 codes)
     wg_ms, wg_n = kern["bwd_wgrad"]
     wg_s = wg_ms / max(wg_n, 1) / 1e3
-    wg_bytes = n * 3 * H * I * 4 + rows * (3 * H + 3 * I) * wb
+    wg_bytes = n * 3 * H * I * 4 + rows * (2 * H + 3 * I) * wb
     wg_flops = 3 * 2 * rows * H * I
     roofline = {"bound": "hbm", "achieved": round(wg_bytes / wg_s / 1e9, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(wg_bytes / wg_s / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(f"backward_{args.backward_shape}_{c.w_dtype}"),
-                "kernel": "bwd_wgrad (dW_down, dW_gate, dW_up launches)",
+                "kernel": "bwd_wgrad (dW_down, dW_gate, dW_up)",
                 "kernel_us": round(wg_s * 1e6, 2), "alg_bytes_per_launch": int(wg_bytes),
                 "alg_flops_per_launch": int(wg_flops),
                 "mfma_frac": round(wg_flops / wg_s / 1e12 / mfma_peak, 4)}
