@@ -40,19 +40,19 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
-    "decode": {"src_sha256": "1548235720ad8555eb6f6ba41963e92d279bf399b54c926ff6e5ab3e38d1cb8a",
-              "fetch_kib": 8152847.6, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "87067b36c57a104b5b0fc9a56fe9a9822c02f2165b97d201c90f28d8c9b3d2c4",
-               "fetch_kib": 12193395.5, "write_kib": 294912.0},
-    "backward_prefill_bf16": {"src_sha256": "300f12aa2ed1c421c3e3d2ee62ada241ac861ab449ebe302d35019cfaf106525",
-                             "fetch_kib": 8764995.2, "write_kib": 44216125.6},
+    "decode": {"src_sha256": "6b57225de6925b7cae7df903c7219550068387215c4cc7e2f6776151bf9b6faa",
+             "fetch_kib": 8153092.2, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "85c3e329c1f1371f3811f9a95208de880753021de71c1f1a80d7997cb0eee7e2",
+              "fetch_kib": 12174213.4, "write_kib": 294912.0},
+    "backward_prefill_bf16": {"src_sha256": "1aac6507fbf16b206b544848b190c0e076903a2199f98e5669a2080ec8b02ee6",
+                            "fetch_kib": 6452700.6, "write_kib": 44215261.0},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "87067b36c57a104b5b0fc9a56fe9a9822c02f2165b97d201c90f28d8c9b3d2c4",
-                "busy": 0.58, "clock_ghz": 1.47, "executed_bf16_tflop": 4.56},
+    "prefill": {"src_sha256": "85c3e329c1f1371f3811f9a95208de880753021de71c1f1a80d7997cb0eee7e2",
+                "busy": 0.573, "clock_ghz": 1.52, "executed_bf16_tflop": 4.56},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
