@@ -999,12 +999,16 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   if (t >= T) return;
   if (dgp != nullptr) {
     // dg_k = <dy, Y_k> = <dy W_down, H_k> = <dH_k, H_k> / g_k, dH_k = g_k dy W_down
-    // (the data-gradient GEMM's per-tile row sums, added in tile order)
+    // (the data-gradient GEMM's per-tile row sums, added in tile order).  A gate
+    // of exactly 0 (its sigmoid underflowed) gets dg_k = 0: below, dg_k enters
+    // only through g_k dg_k and through ds_k, which is scaled by s_k (1 - s_k) = 0,
+    // so every logit gradient is the same as with the true <dy, Y_k>.
     for (int k = 0; k < K; ++k) {
       const long long r = slot[t * K + k];
       float a = 0.f;
       for (int p = 0; p < n_part; ++p) a += dgp[p * rows_total + r];
-      dg[t * K + k] = a / gate[t * K + k];
+      const float gk = gate[t * K + k];
+      dg[t * K + k] = gk > 0.f ? a / gk : 0.f;
     }
   }
   float s[32];

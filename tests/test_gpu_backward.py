@@ -105,6 +105,46 @@ def test_backward_is_deterministic():
         assert torch.equal(u, v)
 
 
+def test_backward_with_an_underflowed_gate():
+    """A chosen expert whose float32 sigmoid underflows to 0 (gate exactly 0).
+
+    The GPU forms dg_k = <dH_k, H_k> / g_k from the data-gradient GEMM; at g_k =
+    0 it takes dg_k = 0, which leaves every logit gradient as the true <dy, Y_k>
+    would (dg_k enters them only through g_k dg_k and s_k (1 - s_k)).  Inputs:
+    mid_skew (x[:, 0] = 1), expert 5's router column -120 e_0 (logit -120 for
+    every token: float32 sigmoid 0, float64 7.7e-53), its bias +10 (chosen by
+    every token).  The oracle runs in float64 on the same inputs."""
+    c = S.get_config("mid_skew", T=800)
+    say(f"backward, underflowed gate: mid_skew T={c.T}")
+    e0 = 5
+    wr = S.gen_router(c, "cpu").clone()
+    wr[:, e0] = 0.0
+    wr[0, e0] = -120.0
+    b = S.gen_bias(c, "cpu").clone()
+    b[e0] = 10.0
+    gi = GpuInputs(c)
+    gi.wr = wr.to(DEV)
+    gi.b = b.to(DEV)
+    counts = gi.run_route()["counts"].cpu().numpy()
+    assert counts[e0] == c.T
+    dy = _dy(c)
+    dx, dwr, dwg, dwu, dwd = _run(gi, dy)
+    assert bool(torch.isfinite(dx.float()).all()) and bool(torch.isfinite(dwr).all())
+    ref = O.backward(O.lift(S.gen_x(c, device="cpu")), O.lift(wr), b.numpy(), cpu_expert_source(c),
+                     O.lift(dy), n_groups=c.n_groups, topk_groups=c.topk_groups, topk=c.topk,
+                     group_topn=c.group_topn, n_shared=c.n_shared, grad_experts=[e0, c.n_experts])
+    rows = _row_rel(dx.float().cpu().numpy(), ref.dx)
+    wr_err = _rel_f(dwr.cpu().numpy(), ref.dw_router)
+    sh = c.n_experts
+    mats = [_rel_f(got[sh].cpu().numpy(), want) for got, want in zip((dwg, dwu, dwd), ref.dw[sh])]
+    say(f"underflowed gate: dx max row rel {rows.max():.3e}; dW_r rel {wr_err:.3e}; shared dW max "
+        f"rel {max(mats):.3e}")
+    assert rows.max() <= TOL and wr_err <= TOL and max(mats) <= TOL
+    # expert e0's gradients carry the factor g = 0 (float64: 1e-53 of the others)
+    for got, want in zip((dwg, dwu, dwd), ref.dw[e0]):
+        assert float(got[e0].abs().max()) == 0.0 and float(np.abs(want).max()) < 1e-40
+
+
 @pytest.mark.parametrize("name", ["decode", "prefill"])
 def test_v3_backward_sampled(name):
     c = S.get_config(name)
