@@ -18,7 +18,7 @@ struct BwdArgs {
   const bf16_t* w_up;         // [E+S][I][H]
   const bf16_t* w_down;       // [E+S][H][I]
   bf16_t* xst;                // [rows][H] x in staged-row order
-  bf16_t* gst;                // [rows][I] recomputed X W_gate^T
+  bf16_t* gst;                // [rows][I] recomputed X W_gate^T (the forward's gated GEMM)
   bf16_t* ust;                // [rows][I] recomputed X W_up^T
   bf16_t* hst;                // [rows][I] recomputed SiLU(G) * U
   bf16_t* yst;                // [rows][H] recomputed expert outputs
@@ -43,10 +43,10 @@ struct BwdArgs {
 
 int bwd_max_row_tiles(int T, int K, int E, int S);
 
-// One stage of the backward (0 gather x, 1 SwiGLU, 2 combine backward and tile
-// prefixes, 3 router backward, 4 dH GEMM, 5 dX GEMM, 6 weight-gradient GEMMs,
-// 7 dW_r, 8 dx); P / ks: router partials and their count.  With dgp, stage 3
-// runs after stage 4.
+// One stage of the backward (0 gather x, 2 combine backward and tile prefixes,
+// 3 router backward, 4 dH GEMM, 5 dX GEMM, 6 weight-gradient GEMMs, 7 dW_r,
+// 8 dx; G, U and H come from the forward's gated GEMM); P / ks: router
+// partials and their count.  With dgp, stage 3 runs after stage 4.
 hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, const int32_t* idx,
                                    const int32_t* slot, const float* gate, const float* w_router,
                                    const bf16_t* dy, bf16_t* dx, float* dw_router, hipStream_t st,

@@ -890,16 +890,6 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restri
   for (int c = threadIdx.x; c < H / 8; c += 256) d[c] = s[c];
 }
 
-// H = SiLU(G) * U, elementwise over the staged rows
-__global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ gst,
-                                                     const bf16_t* __restrict__ ust, long long n,
-                                                     bf16_t* __restrict__ hst) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float G = bf16_to_f32(gst[i]), U = bf16_to_f32(ust[i]);
-  hst[i] = f32_to_bf16(G * sigm(G) * U);
-}
-
 // Per token t: for each chosen expert k, the gate gradient dg = <dy_t, Y_k[t]>
 // (fixed-order block reduction) and the expert's output gradient g_k dy_t; the
 // shared expert's output gradient is dy_t itself.  dyst == nullptr: gate
@@ -1177,10 +1167,6 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
     case 0:  // expert-ordered copy of x
       hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(256), 0, st, g.x, g.perm, T, g.TK, S,
                          H, g.xst);
-      break;
-    case 1:  // H from the recomputed G and U
-      hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned((size_t(rows) * I + 255) / 256)), dim3(256),
-                         0, st, g.gst, g.ust, (long long)rows * I, g.hst);
       break;
     case 2:  // combine backward (without dgp; with dgp only the output gradients), tile prefixes
       hipLaunchKernelGGL(combine_bwd_kernel, dim3(T), dim3(256), 0, st, dy,

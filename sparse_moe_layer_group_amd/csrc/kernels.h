@@ -49,9 +49,13 @@ struct StreamArgs {
   const int32_t* offsets;
   const int32_t* chunk_start; // [E+S+1] prefix of 16-row chunks of streamed experts
   int E, n_exp, T, TK, N, K;
+  bf16_t* out_g;              // mode 2 (gated, for the backward): G and U too, [rows][N]
+  bf16_t* out_u;
 };
 constexpr int kMaxStreamExperts = 1024;  // n_exp bound of the streaming GEMM's LDS tables
-hipError_t launch_stream_gemm(const StreamArgs& g, bool gated, int n_blocks, hipStream_t st);
+// mode 0: out = A W0^T; 1: out = SiLU(x W0^T) * (x W1^T), x rows gathered
+// through perm; 2: as 1, and the two products also to out_g and out_u
+hipError_t launch_stream_gemm(const StreamArgs& g, int mode, int n_blocks, hipStream_t st);
 
 // LDS-tiled GEMM for experts with many rows (tile_gemm.hip), bf16 only;
 // kTileM-row tiles, gate/up column tiles of 128, down column tiles of 256
@@ -65,12 +69,14 @@ struct TileArgs {
   const int32_t* offsets;
   const int32_t* mt_start;    // [E+S+1] prefix of kTileM-row tiles of tiled experts
   int E, n_exp, T, TK, N, K;
+  bf16_t* out_g;              // mode 2 (gated, for the backward): G and U too, [rows][N]
+  bf16_t* out_u;
 };
 #ifndef MOE_TILE_MBW
 #define MOE_TILE_MBW 5  // 32-row MFMA blocks per wave of the tiled GEMM (2 waves along M)
 #endif
 constexpr int kTileM = 64 * MOE_TILE_MBW;
-hipError_t launch_tile_gemm(const TileArgs& g, bool gated, int max_mtiles, hipStream_t st);
+hipError_t launch_tile_gemm(const TileArgs& g, int mode, int max_mtiles, hipStream_t st);  // modes as above
 
 int gemm_tile_m();
 template <typename TE>

@@ -296,14 +296,14 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
                          static_cast<const bf16_t*>(w->w_gate), static_cast<const bf16_t*>(w->w_up),
                          reinterpret_cast<bf16_t*>(hst), r.perm, r.counts, r.offsets, chunk_start,
                          E, E + S, T, TK, I, H};
-      hipError_t err = moe::launch_stream_gemm(sa, true, stream_blocks(I / 64), st);
+      hipError_t err = moe::launch_stream_gemm(sa, 1, stream_blocks(I / 64), st);
       if (err != hipSuccess || !tiles) return err;
     }
     if (big) {
       moe::TileArgs ta{reinterpret_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w->w_gate),
                        static_cast<const bf16_t*>(w->w_up), reinterpret_cast<bf16_t*>(hst), r.perm,
                        r.counts, r.offsets, mt_start, E, E + S, T, TK, I, H};
-      return moe::launch_tile_gemm(ta, true, max_mt, st);
+      return moe::launch_tile_gemm(ta, 1, max_mt, st);
     }
     return moe::launch_gemm<TE>(g1, true, max_mt, 4 * cu_count(), st);
   }));
@@ -315,14 +315,14 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
                          static_cast<const bf16_t*>(w->w_down), nullptr,
                          reinterpret_cast<bf16_t*>(yst), r.perm, r.counts, r.offsets, chunk_start,
                          E, E + S, T, TK, H, I};
-      hipError_t err = moe::launch_stream_gemm(sa, false, stream_blocks(H / 128), st);
+      hipError_t err = moe::launch_stream_gemm(sa, 0, stream_blocks(H / 128), st);
       if (err != hipSuccess || !tiles) return err;
     }
     if (big) {
       moe::TileArgs ta{reinterpret_cast<const bf16_t*>(hst), static_cast<const bf16_t*>(w->w_down),
                        nullptr, reinterpret_cast<bf16_t*>(yst), r.perm, r.counts, r.offsets,
                        mt_start, E, E + S, T, TK, H, I};
-      return moe::launch_tile_gemm(ta, false, max_mt, st);
+      return moe::launch_tile_gemm(ta, 0, max_mt, st);
     }
     return moe::launch_gemm<TE>(g2, false, max_mt, 4 * cu_count(), st);
   }));
@@ -463,11 +463,12 @@ int validate_bwd(const moe_cfg* c, int64_t T) {
   return MOE_OK;
 }
 
-// plain (non-gated) expert GEMM on staged rows, out[row][n] = sum_k a[row][k] w[e][n][k],
-// dispatched like the forward's down GEMM
-int run_plain_gemm(const moe_cfg& c, int T, const bf16_t* a, const bf16_t* w, bf16_t* out, int N,
-                   int Kd, const RoutePtrs& r, void* ws, const Layout& L, hipStream_t st) {
-  const int E = c.n_experts, K = c.topk, S = c.n_shared;
+// the forward's gate/up GEMM for the backward's recompute: x rows gathered through
+// the permutation, H = SiLU(G) * U staged as in the forward, G and U kept as well
+int run_gate_up_keep(const moe_cfg& c, int T, const bf16_t* x, const bf16_t* wg, const bf16_t* wu,
+                     bf16_t* h, bf16_t* gst, bf16_t* ust, const RoutePtrs& r, void* ws,
+                     const Layout& L, hipStream_t st) {
+  const int E = c.n_experts, K = c.topk, S = c.n_shared, H = c.hidden, I = c.inter;
   const int TK = T * K;
   const int bm = tile_rows(c);
   const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
@@ -475,18 +476,18 @@ int run_plain_gemm(const moe_cfg& c, int T, const bf16_t* a, const bf16_t* w, bf
   const bool streams = smax >= 0, tiles = smax < T;
   if (streams) {
     const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
-    const long long waves = chunks * (N / 128);
+    const long long waves = chunks * (I / 64);
     const int blocks =
         int(std::max<long long>(1, std::min<long long>((waves + 3) / 4, (long long)cu_count())));
-    moe::StreamArgs sa{a, w, nullptr, out, r.perm, r.counts, r.offsets,
-                       at<int32_t>(ws, L.chunk_start), E, E + S, T, TK, N, Kd};
-    hipError_t err = moe::launch_stream_gemm(sa, false, blocks, st);
+    moe::StreamArgs sa{x, wg, wu, h, r.perm, r.counts, r.offsets, at<int32_t>(ws, L.chunk_start),
+                       E, E + S, T, TK, I, H, gst, ust};
+    hipError_t err = moe::launch_stream_gemm(sa, 2, blocks, st);
     if (err != hipSuccess) return MOE_ERR_HIP;
     if (!tiles) return MOE_OK;
   }
-  moe::TileArgs ta{a, w, nullptr, out, r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_start),
-                   E, E + S, T, TK, N, Kd};
-  return moe::launch_tile_gemm(ta, false, max_mt, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  moe::TileArgs ta{x, wg, wu, h, r.perm, r.counts, r.offsets, at<int32_t>(ws, L.mt_start),
+                   E, E + S, T, TK, I, H, gst, ust};
+  return moe::launch_tile_gemm(ta, 2, max_mt, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
@@ -547,15 +548,15 @@ int run_backward(const moe_cfg& c, int T, const bf16_t* x, const float* wr, cons
   auto stage = [&](int s) {
     return moe::launch_backward_kernels(g, P, ks, r.idx, r.slot, r.gate, wr, dy, dx, dwr, st, s);
   };
-  // recompute the forward's expert intermediates from x (G, U and H; Y is not
-  // needed: the gate gradients <dy, Y_k> = <dH_k, H_k> / g_k come out of the dH GEMM)
+  // recompute the forward's expert intermediates from x (G, U and H in one gated
+  // GEMM; Y is not needed: the gate gradients <dy, Y_k> = <dH_k, H_k> / g_k come
+  // out of the dH GEMM); X rows staged for the weight gradients
   MOE_TRY(timed(K_BWD_RECOMPUTE, st, [&]() -> hipError_t {
     hipError_t err = stage(0);
     if (err != hipSuccess) return err;
-    if (run_plain_gemm(c, T, g.xst, g.w_gate, g.gst, I, H, r, ws, L, st) != MOE_OK ||
-        run_plain_gemm(c, T, g.xst, g.w_up, g.ust, I, H, r, ws, L, st) != MOE_OK)
-      return hipErrorLaunchFailure;
-    return stage(1);
+    return run_gate_up_keep(c, T, x, g.w_gate, g.w_up, g.hst, g.gst, g.ust, r, ws, L, st) == MOE_OK
+               ? hipSuccess
+               : hipErrorLaunchFailure;
   }));
   MOE_TRY(timed(K_BWD_COMBINE, st, [&] { return stage(2); }));  // g dy, tile prefixes
   MOE_TRY(timed(K_BWD_DH, st, [&] { return stage(4); }));       // dH, dG, dU, gate-gradient sums

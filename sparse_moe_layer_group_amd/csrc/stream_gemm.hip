@@ -27,7 +27,8 @@
 //
 // Column map: gated slices hold 64 output columns; weight row of tile j
 // (j = 0..3 gate, 4..7 up) for lane l is c0 + 4*(l%16) + (j%4), so a lane
-// owns four adjacent output columns.  Plain slices hold 128 columns: row
+// owns four adjacent output columns (mode 2, the backward's recompute, stores
+// gate and up as well as SiLU(gate) * up).  Plain slices hold 128 columns: row
 // c0 + 8*(l%16) + j, eight adjacent output columns per lane.
 #include "common.h"
 #include "kernels.h"
@@ -70,8 +71,9 @@ struct StreamTask {
   int e, row_base, m0, rows, slice;
 };
 
-template <bool GATED>
+template <int MODE>
 __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
+  constexpr bool GATED = MODE != 0;
   // chunk prefix, counts and offsets in LDS: the per-task expert search must
   // not wait on dependent global loads between two tasks' weight streams
   __shared__ int cs_s[kMaxStreamExperts + 1];
@@ -180,6 +182,16 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
         pk.y = uint32_t(f32_to_bf16(siluf(acc[2][t]) * acc[6][t])) |
                (uint32_t(f32_to_bf16(siluf(acc[3][t]) * acc[7][t])) << 16);
         *reinterpret_cast<uint2*>(dst + c) = pk;
+        if (MODE == 2) {  // the backward keeps G and U as well
+          const size_t o = (size_t)(row_base + m) * g.N + c;
+          uint2 pg, pu;
+          pg.x = uint32_t(f32_to_bf16(acc[0][t])) | (uint32_t(f32_to_bf16(acc[1][t])) << 16);
+          pg.y = uint32_t(f32_to_bf16(acc[2][t])) | (uint32_t(f32_to_bf16(acc[3][t])) << 16);
+          pu.x = uint32_t(f32_to_bf16(acc[4][t])) | (uint32_t(f32_to_bf16(acc[5][t])) << 16);
+          pu.y = uint32_t(f32_to_bf16(acc[6][t])) | (uint32_t(f32_to_bf16(acc[7][t])) << 16);
+          *reinterpret_cast<uint2*>(g.out_g + o) = pg;
+          *reinterpret_cast<uint2*>(g.out_u + o) = pu;
+        }
       } else {
         const int c = slice * 128 + 8 * (lane & 15);
         u32x4 pk;
@@ -195,10 +207,12 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
   }
 }
 
-hipError_t launch_stream_gemm(const StreamArgs& g, bool gated, int n_blocks, hipStream_t st) {
+hipError_t launch_stream_gemm(const StreamArgs& g, int mode, int n_blocks, hipStream_t st) {
   if (g.n_exp > kMaxStreamExperts) return hipErrorInvalidValue;
-  if (gated) hipLaunchKernelGGL(stream_gemm_kernel<true>, dim3(n_blocks), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL(stream_gemm_kernel<false>, dim3(n_blocks), dim3(256), 0, st, g);
+  if (mode == 2 && (g.out_g == nullptr || g.out_u == nullptr)) return hipErrorInvalidValue;
+  if (mode == 1) hipLaunchKernelGGL(stream_gemm_kernel<1>, dim3(n_blocks), dim3(256), 0, st, g);
+  else if (mode == 2) hipLaunchKernelGGL(stream_gemm_kernel<2>, dim3(n_blocks), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL(stream_gemm_kernel<0>, dim3(n_blocks), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 // Workgroup tile: kTileM (320) rows x 256 weight rows, K in steps of 64.
 // Gate/up tiles hold 128 columns: weight rows 0..127 come from W_gate and
 // 128..255 from W_up for the same columns, so SiLU(gate) * up is formed in
-// registers.  Down tiles hold 256 columns of W_down.  Eight waves in 2 (rows)
+// registers (mode 2, the backward's recompute, stores gate and up as well).
+// Down tiles hold 256 columns of W_down.  Eight waves in 2 (rows)
 // x 4 (columns), each owning a 160 x 64 sub-tile as 5 x 2
 // v_mfma_f32_32x32x16_bf16 blocks, two waves per SIMD.  32-row blocks past
 // the expert's row count are skipped per wave.
@@ -105,8 +106,9 @@ constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0
 // (The tile configuration is a set of namespace constants rather than
 // template parameters: with more than one template parameter this compiler
 // does not emit the host-side launch stubs.)
-template <bool GATED>
+template <int MODE>
 __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
+  constexpr bool GATED = MODE != 0;
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* As = smem;                  // [NSA][TBM][TBK]
   bf16_t* Bs = smem + NSA * ASTAGE;   // [NSB][TBN][TBK]
@@ -357,8 +359,13 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 32 * MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r < rows && col < g.N) {
+          const size_t o = (size_t)(row_base + m0 + r) * g.N + col;
           const float val = GATED ? siluf(acc[i][j][v]) * acc[i][j + NJ / 2][v] : acc[i][j][v];
-          g.out[(size_t)(row_base + m0 + r) * g.N + col] = f32_to_bf16(val);
+          g.out[o] = f32_to_bf16(val);
+          if (MODE == 2) {  // the backward keeps G and U as well
+            g.out_g[o] = f32_to_bf16(acc[i][j][v]);
+            g.out_u[o] = f32_to_bf16(acc[i][j + NJ / 2][v]);
+          }
         }
       }
     }
@@ -367,8 +374,9 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
 
 size_t tile_gemm_lds_bytes() { return size_t(NSA * ASTAGE + NSB * BSTAGE) * sizeof(bf16_t); }
 
-template <bool GATED>
+template <int MODE>
 static hipError_t launch_one(const TileArgs& g, int max_mtiles, hipStream_t st) {
+  constexpr bool GATED = MODE != 0;
   const int n_nt = GATED ? g.N / (TBN / 2) : (g.N + TBN - 1) / TBN;
   // one workgroup per task, up to the largest task count the routing can
   // produce (workgroups past the actual count exit at once)
@@ -379,17 +387,19 @@ static hipError_t launch_one(const TileArgs& g, int max_mtiles, hipStream_t st) 
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&tile_gemm_kernel<GATED>),
+        reinterpret_cast<const void*>(&tile_gemm_kernel<MODE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tile_gemm_kernel<GATED>), dim3((unsigned)blocks), dim3(NTHREAD), lds, st, g);
+  hipLaunchKernelGGL((tile_gemm_kernel<MODE>), dim3((unsigned)blocks), dim3(NTHREAD), lds, st, g);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_gemm(const TileArgs& g, bool gated, int max_mtiles, hipStream_t st) {
-  return gated ? launch_one<true>(g, max_mtiles, st) : launch_one<false>(g, max_mtiles, st);
+hipError_t launch_tile_gemm(const TileArgs& g, int mode, int max_mtiles, hipStream_t st) {
+  if (mode == 2 && (g.out_g == nullptr || g.out_u == nullptr)) return hipErrorInvalidValue;
+  if (mode == 2) return launch_one<2>(g, max_mtiles, st);
+  return mode == 1 ? launch_one<1>(g, max_mtiles, st) : launch_one<0>(g, max_mtiles, st);
 }
 
 }  // namespace moe
