@@ -347,7 +347,50 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
   }
 
   // ---- epilogue.  32x32 accumulator v of lane l: row 8*(v/4) + 4*(l/32) + v%4,
-  // column l%32
+  // column l%32.
+  if constexpr (MODE != 2) {
+    // Through LDS, one 32-row block at a time in a slot of each wave's own,
+    // so that every store is 16 bytes per lane and whole row pieces of the
+    // wave's columns (128 bytes for the down GEMM, 64 for gate/up), 8x fewer
+    // store instructions than 2 bytes per lane from the accumulators.  At
+    // 8192 tokens, on one box: down 2.56 -> 2.51 ms, gate/up 4.69 -> 4.66 ms.
+    // (The stores, done after the main loop, cost about 0.45 ms of the down
+    // GEMM either way: 2.11 ms with them switched off.)
+    constexpr int OJ = GATED ? NJ / 2 : NJ;   // 32-column output blocks per wave
+    constexpr int OB = 64 * OJ;               // output bytes per row and wave
+    constexpr int PITCH = OB + 16;            // staging row bytes (rows r, r + 4 in other banks)
+    constexpr int LPR = OB / 16;              // lanes per staged row
+    constexpr int RPI = 64 / LPR;             // rows per store instruction
+    const int col0 = GATED ? (nt * (TBN / 2) + wn * (TBN / 2 / WN)) : (nt * TBN + wn * (TBN / WN));
+    const bool cols_ok = col0 < g.N;          // a down tile may be half past N
+    __syncthreads();                          // every wave is done with the stages
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_u8* stg = (lds_u8*)smem + wave * 32 * PITCH;
+#pragma unroll
+    for (int i = 0; i < MBW; ++i) {
+      if (i >= mact) continue;  // uniform
+#pragma unroll
+      for (int j = 0; j < OJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float val = GATED ? siluf(acc[i][j][v]) * acc[i][j + NJ / 2][v] : acc[i][j][v];
+          const int r32 = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          *(__attribute__((address_space(3))) bf16_t*)(stg + r32 * PITCH + 2 * (32 * j + (lane & 31))) =
+              f32_to_bf16(val);
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int rr = q * RPI + lane / LPR, cb = 16 * (lane % LPR);
+        const u32x4 val = *(__attribute__((address_space(3))) const u32x4*)(stg + rr * PITCH + cb);
+        const int r = wm * 32 * MBW + 32 * i + rr;
+        if (cols_ok && r < rows)
+          *reinterpret_cast<u32x4*>(g.out + (size_t)(row_base + m0 + r) * g.N + col0 + cb / 2) = val;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
     if (i >= mact) continue;  // uniform; keeps the loop unrolled
