@@ -41,18 +41,18 @@ COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buff
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
     "decode": {"src_sha256": "4a4e21a09259d43cdd3d4ecfb2c414c80c9a5011bc8473fa60e8c3652ae2eef3",
-             "fetch_kib": 8154443.9, "write_kib": 9216.0},
-    "prefill": {"src_sha256": "fa14f24d3259ed3fd91dfadc8e623dd6e409821d2eaaa74076326dcca9d8072f",
-              "fetch_kib": 12184606.2, "write_kib": 294912.0},
+             "fetch_kib": 8155177.8, "write_kib": 9216.0},
+    "prefill": {"src_sha256": "d25fe2c24e864f3934ea59142c945a682c000c538d8bda9bd03bde984c3eb695",
+              "fetch_kib": 12205459.8, "write_kib": 294912.0},
     "backward_prefill_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
-                            "fetch_kib": 6422749.9, "write_kib": 44215336.4},
+                            "fetch_kib": 6394862.8, "write_kib": 44214735.7},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "fa14f24d3259ed3fd91dfadc8e623dd6e409821d2eaaa74076326dcca9d8072f",
-                "busy": 0.562, "clock_ghz": 1.6, "executed_bf16_tflop": 4.56},
+    "prefill": {"src_sha256": "d25fe2c24e864f3934ea59142c945a682c000c538d8bda9bd03bde984c3eb695",
+                "busy": 0.577, "clock_ghz": 1.53, "executed_bf16_tflop": 4.56},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
