@@ -70,12 +70,14 @@ def _row_rel(a, b):
 # kernel with one tile; T=65 and 1: the 128-row kernel
 # mid T=3000 and mid_skew T=800 take the persistent weight-gradient kernel (more
 # than 64 rows per routed expert); mid_skew T=800 has two experts without rows
-# (all-zero gradient tiles) and one with 792 rows (25 k-steps)
-@pytest.mark.parametrize("name,T", [("mid", 300), ("mid", 65), ("mid", 1), ("mid_skew", 300),
-                                    ("mid", 3000), ("mid_skew", 800)])
-def test_backward_parity(name, T):
-    c = S.get_config(name, T=T)
-    say(f"backward parity: {name} T={T}")
+# (all-zero gradient tiles) and one with 792 rows (25 k-steps); mid T=800 without
+# a shared expert: no shared rows, tiles or gradients anywhere in the backward
+@pytest.mark.parametrize("name,T,kw", [("mid", 300, {}), ("mid", 65, {}), ("mid", 1, {}),
+                                       ("mid_skew", 300, {}), ("mid", 3000, {}), ("mid_skew", 800, {}),
+                                       ("mid", 800, {"n_shared": 0})])
+def test_backward_parity(name, T, kw):
+    c = S.get_config(name, T=T, **kw)
+    say(f"backward parity: {name} T={T} {kw}")
     gi = GpuInputs(c)
     dy = _dy(c)
     dx, dwr, dwg, dwu, dwd = _run(gi, dy)
