@@ -77,17 +77,18 @@ def _fmt(rows, mats, wr):
 
 # T=1200: 114-191 rows per routed expert, so every expert's 128x1 tiles span two
 # row blocks with a partial last one
-@pytest.mark.parametrize("T", [300, 65, 1, 1200])
-def test_fp8_backward_parity(T):
-    c = S.get_config("mid_fp8", T=T)
-    say(f"fp8 backward parity: mid_fp8 T={T}")
+# T=1200 without a shared expert: no shared rows, 128x1 tiles or gradients
+@pytest.mark.parametrize("T,kw", [(300, {}), (65, {}), (1, {}), (1200, {}), (1200, {"n_shared": 0})])
+def test_fp8_backward_parity(T, kw):
+    c = S.get_config("mid_fp8", T=T, **kw)
+    say(f"fp8 backward parity: mid_fp8 T={T} {kw}")
     gi = GpuInputs(c)
     dy = _dy(c)
     out = _run(gi, dy)
     emu = _oracle(c, dy, fp8_emulation=True)
     got = _errs(emu, *out)
-    say(f"mid_fp8 T={T} vs emulation: {_fmt(*got)}")
-    say(f"mid_fp8 T={T} vs the exact backward: {_fmt(*_errs(_oracle(c, dy), *out))}")
+    say(f"mid_fp8 T={T} {kw} vs emulation: {_fmt(*got)}")
+    say(f"mid_fp8 T={T} {kw} vs the exact backward: {_fmt(*_errs(_oracle(c, dy), *out))}")
     _check(*got)
 
 
