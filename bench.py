@@ -46,6 +46,8 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
               "fetch_kib": 12205459.8, "write_kib": 294912.0},
     "backward_prefill_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
                             "fetch_kib": 6394862.8, "write_kib": 44214735.7},
+    "backward_decode_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
+                            "fetch_kib": 85678.5, "write_kib": 44238395.1},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
@@ -62,6 +64,7 @@ KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
                   "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",),
                   # backward: the weight-gradient stage (all its launches in one call)
                   "backward_prefill_bf16": _COMMON_SOURCES + ("bwd.h", "bwd_kernels.hip"),
+                  "backward_decode_bf16": _COMMON_SOURCES + ("bwd.h", "bwd_kernels.hip"),
                   "backward_prefill_e4m3": _COMMON_SOURCES + ("bwd.h", "bwd_fp8_kernels.hip")}
 
 
