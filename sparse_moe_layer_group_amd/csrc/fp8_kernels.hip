@@ -378,19 +378,31 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
       }
     }
   } else {
+    // through a slot of each wave's own in LDS, 16 rows at a time: one 16-byte
+    // store per lane writes 16 rows x the wave's 64 bytes (2-byte stores from
+    // the accumulators write 32-byte pieces)
+    constexpr int PITCH = 64 + 16;  // staging row bytes
+    typedef __attribute__((address_space(3))) uint8_t lds8;
+    __syncthreads();  // every wave is done with the staged operands
+    lds8* stg = (lds8*)smem8 + wave * 16 * PITCH;
+    const int col0 = nt * FS_TBN + 32 * wave;
+    const bool cols_ok = col0 < g.N;  // a down tile may be half past N
 #pragma unroll
     for (int i = 0; i < FS_RB; ++i) {
       if (2 * mact <= i) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = nt * FS_TBN + 32 * wave + 16 * j + c16;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = 16 * i + 4 * g4 + v;
-          if (r < rows && col < g.N)
-            g.out16[(size_t)(row_base + m0 + r) * g.N + col] = f32_to_bf16(acc[i][j][v]);
-        }
-      }
+        for (int v = 0; v < 4; ++v)
+          *(__attribute__((address_space(3))) bf16_t*)(stg + (4 * g4 + v) * PITCH + 2 * (16 * j + c16)) =
+              f32_to_bf16(acc[i][j][v]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int rr = lane >> 2, cb = 16 * (lane & 3);
+      const u32x4 val = *(__attribute__((address_space(3))) const u32x4*)(stg + rr * PITCH + cb);
+      const int r = 16 * i + rr;
+      if (cols_ok && r < rows)
+        *reinterpret_cast<u32x4*>(g.out16 + (size_t)(row_base + m0 + r) * g.N + col0 + cb / 2) = val;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 }
