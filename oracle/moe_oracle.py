@@ -45,6 +45,11 @@ Parity status of each function (what pins it in tests/test_oracle_*.py):
                         of the fixed-routing layer; zero router gradient with
                         one routed expert; linearity in dy)
   quantize_128x1        pinned (equals quantize_1x128 of the transpose)
+  forward(act_quant) / expert_ffn_fp8  pinned (with the identity quantiser it
+                        is the plain forward up to the float32 rounding of H;
+                        scalar-loop brute force of the 1x128 quantisation of x
+                        and H, with torch's float8_e4m3fn as the encoder, on
+                        tiny E4M3 layers with outliers)
   backward(fp8_emulation) and expert_*_fp8  pinned (with the quantisers
                         replaced by the identity it equals the pinned backward;
                         token isolation of dx; exact column equivariance of
@@ -255,6 +260,25 @@ def expert_ffn(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) ->
     return (silu(G) * U) @ wd.T
 
 
+def expert_ffn_fp8(Xq: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+                   act_quant: Optional[Callable[[np.ndarray], np.ndarray]] = None) -> np.ndarray:
+    """One SwiGLU expert on the E4M3 forward path, float64.
+
+    [V3] §2.2: the inputs of every expert GEMM are E4M3 with one scale per
+    1x128 activation tile; the products are accumulated at high precision.
+    ``Xq`` holds the expert's input rows already quantised (the layer input is
+    quantised once, before any expert); ``wg``, ``wu``, ``wd`` are the
+    dequantised weights.  Reading: G = Xq W_gate^T and U = Xq W_up^T are exact
+    products; H = SiLU(G) * U is rounded to float32 (the value a float32
+    accumulator holds when it is quantised) and quantised 1x128 along the
+    intermediate dimension as the down projection's input; Y = Q(H) W_down^T.
+    ``act_quant`` is the quantiser (``fake_quant_1x128`` when None).
+    """
+    q = fake_quant_1x128 if act_quant is None else act_quant
+    Hh = (silu(Xq @ wg.T) * (Xq @ wu.T)).astype(F32).astype(F64)
+    return q(Hh) @ wd.T
+
+
 ExpertSource = Callable[[int], Dict[str, np.ndarray]]
 
 
@@ -298,7 +322,9 @@ def forward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: ExpertS
 
     ``experts(e)`` returns expert e's weights (routed 0..E-1, shared = E).
     ``act_quant`` (optional) maps a float64 activation matrix to its quantised
-    value; it is applied to the expert inputs and to the SwiGLU output.
+    value (``fake_quant_1x128`` for the E4M3 path of [V3] §2.2): it is applied
+    once to the layer input x, and each expert then runs ``expert_ffn_fp8``
+    with it.
     """
     T = x64.shape[0]
     E = wr64.shape[1]
@@ -315,8 +341,7 @@ def forward(x64: np.ndarray, wr64: np.ndarray, b32: np.ndarray, experts: ExpertS
         wg, wu, wd = expert_f64(w)
         if act_quant is None:
             return expert_ffn(X, wg, wu, wd)
-        Hq = act_quant((silu(X @ wg.T) * (X @ wu.T)).astype(F32).astype(F64))
-        return Hq @ wd.T
+        return expert_ffn_fp8(X, wg, wu, wd, act_quant)
 
     # routed experts in ascending id, each on the requested tokens that chose
     # it, so every token accumulates its K terms in ascending expert order

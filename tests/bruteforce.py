@@ -76,3 +76,49 @@ def swiglu_loop(xv, wg, wu, wd):
             acc += float(wd[i, j]) * h[j]
         y[i] = acc
     return np.array(y)
+
+
+def e4m3_slices_loop(v):
+    """Quantise-then-dequantise a vector slice by slice, 128 entries a slice.
+
+    Per slice: amax by a loop; scale = amax / 448 in float32 (1 where that is
+    zero); each entry's float32 quotient v / scale, saturated at +-448, is
+    rounded to an E4M3FN value by torch's float8_e4m3fn conversion (an
+    encoder independent of the oracle's); the result is value * scale in
+    float64.
+    """
+    import torch
+    out = []
+    for s0 in range(0, len(v), 128):
+        sl = [np.float32(a) for a in v[s0:s0 + 128]]
+        amax = np.float32(0.0)
+        for a in sl:
+            if abs(a) > amax:
+                amax = np.float32(abs(a))
+        scale = np.float32(amax / np.float32(448.0))
+        if scale == 0:
+            scale = np.float32(1.0)
+        for a in sl:
+            r = min(max(float(np.float32(a / scale)), -448.0), 448.0)
+            code = torch.tensor([r], dtype=torch.float32).to(torch.float8_e4m3fn)
+            out.append(float(code.to(torch.float64)[0]) * float(scale))
+    return np.array(out)
+
+
+def swiglu_fp8_loop(xv, wg, wu, wd):
+    """One token through one expert on the E4M3 forward path, by loops.
+
+    The token's input is quantised per 1x128 slice; h_j = silu(g_j) * u_j from
+    exact dot products with the quantised input, rounded to float32 and
+    quantised per 1x128 slice; y_i = sum_j wd[i][j] hq_j.
+    """
+    I, H = wg.shape
+    xq = e4m3_slices_loop(xv)
+    h = np.zeros(I, dtype=np.float32)
+    for j in range(I):
+        g = float(np.dot(wg[j], xq))
+        u = float(np.dot(wu[j], xq))
+        e = math.exp(-g) if g > -700.0 else math.inf     # SiLU(g) -> -0 for very negative g
+        h[j] = np.float32(g / (1.0 + e) * u)
+    hq = e4m3_slices_loop(h)
+    return np.array([float(np.dot(wd[i], hq)) for i in range(H)])

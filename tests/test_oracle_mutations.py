@@ -13,6 +13,7 @@ from tests import test_oracle_backward_fp8 as TB8
 from tests import test_oracle_balance as TB
 from tests import test_oracle_ffn as TF
 from tests import test_oracle_fp8 as T8
+from tests import test_oracle_fp8_forward as T8F
 from tests import test_oracle_routing as TR
 
 
@@ -25,7 +26,8 @@ _orig = {n: getattr(M, n) for n in ("group_scores", "biased_scores", "gate_value
                                      "expert_ffn", "bias_update", "router_affinity",
                                      "e4m3_quantize", "select_experts",
                                      "sequence_balance_loss", "dsilu", "gate_backward",
-                                     "expert_backward", "expert_swiglu_input_fp8")}
+                                     "expert_backward", "expert_swiglu_input_fp8",
+                                     "expert_ffn_fp8", "forward")}
 
 
 def m_group_top1(z, n_groups, group_topn):
@@ -155,6 +157,27 @@ def m_q128x1_per_row(a):
     return codes, scales
 
 
+def m_fp8_quant_u_not_h(Xq, wg, wu, wd, act_quant=None):
+    # the up projection quantised instead of the SwiGLU output
+    q = M.fake_quant_1x128 if act_quant is None else act_quant
+    return (M.silu(Xq @ wg.T) * q(Xq @ wu.T)).astype(np.float32).astype(np.float64) @ wd.T
+
+
+def m_fp8_h_128x1(Xq, wg, wu, wd, act_quant=None):
+    # H quantised in 128x1 tiles (down the token rows) instead of 1x128
+    Hh = (M.silu(Xq @ wg.T) * (Xq @ wu.T)).astype(np.float32).astype(np.float64)
+    return M.fake_quant_128x1(Hh) @ wd.T
+
+
+def m_fp8_no_input_quant(*a, **kw):
+    # the layer input x left unquantised (only H goes through the quantiser)
+    q = kw.get("act_quant")
+    if q is not None:
+        H = a[0].shape[1]
+        kw["act_quant"] = lambda v: v if v.shape[1] == H else q(v)
+    return _orig["forward"](*a, **kw)
+
+
 CASES = [
     ("group_scores", m_group_top1, TR.test_selection_matches_subset_enumeration, (0,)),
     ("biased_scores", m_no_bias, TR.test_large_bias_forces_and_excludes_experts, ()),
@@ -179,6 +202,12 @@ CASES = [
     ("expert_backward_fp8", m_fp8_dgrad_dy_exact,
      TB8.test_a_substep_change_of_dy_moves_no_weight_gradient, ()),
     ("quantize_128x1", m_q128x1_per_row, TB8.test_quantize_128x1_is_1x128_of_the_transpose, ()),
+    ("expert_ffn_fp8", m_fp8_quant_u_not_h, T8F.test_emulation_matches_scalar_loop_quantisation,
+     (T8F.FP8_TINY,)),
+    ("expert_ffn_fp8", m_fp8_h_128x1, T8F.test_emulation_matches_scalar_loop_quantisation,
+     (T8F.FP8_TINY,)),
+    ("forward", m_fp8_no_input_quant, T8F.test_emulation_matches_scalar_loop_quantisation,
+     (T8F.FP8_TINY,)),
 ]
 
 
