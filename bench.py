@@ -1,6 +1,8 @@
 """Benchmark of the MI355X DeepSeekMoE layer forward (one GPU).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew|fp8]
+    python bench.py --workload fp8 --save-inputs DIR   # write the inputs, then ...
+    python bench.py --workload fp8 --load-inputs DIR   # ... time them without generator kernels
     python bench.py --copy-calibration          # plain copy of known size, for HBM counters
     python bench.py --summarize-profile DIR     # text summary of rocprofv3 CSV output
 
@@ -9,10 +11,14 @@ permutation, routed + shared SwiGLU experts, gated combine) over one batch of
 synthetic V3-shaped input already resident in HBM.  Prints one JSON line.
 
 The default workload is the decode batch (T=256, bf16 weights): the
-configuration the headline metric is quoted on.  Kernel durations come from
-HIP events recorded by the library around each launch on the same stream,
-over the timed steps.  The CPU baseline is the float64 oracle timed on a
-bounded sample of the same workload on this host's cores.
+configuration the headline metric is quoted on, which gives `value`.  The
+same line then carries `prefill` (T=8192, MFMA roofline), `skew` (T=4096,
+200 loss-free bias steps with the per-step load ratio) and `fp8` (T=4096,
+E4M3 weights) objects, each timed the same way on its own inputs
+(`--no-extra` skips them).  Kernel durations come from HIP events recorded by
+the library around each launch on the same stream, over the timed steps.  The
+CPU baseline is the float64 oracle timed on a bounded sample of the decode
+workload on this host's cores.
 """
 import argparse
 import collections
@@ -156,6 +162,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "fp8", "backward"])
+    ap.add_argument("--no-extra", action="store_true",
+                    help="decode workload: skip the prefill, skew and fp8 objects of the line")
     ap.add_argument("--backward-shape", default="prefill", choices=["decode", "prefill"],
                     help="backward workload: batch shape (prefill T=8192 or decode T=256)")
     ap.add_argument("--backward-weights", default="bf16", choices=["bf16", "e4m3"],
@@ -165,6 +173,11 @@ def main():
                     help="skew workload: bias-update steps (forward timed at first, middle, last)")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens in the CPU oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--save-inputs", default=None, metavar="DIR",
+                    help="generate the workload's inputs on the GPU, write them under DIR and exit")
+    ap.add_argument("--load-inputs", default=None, metavar="DIR",
+                    help="read the workload's inputs from DIR (written by --save-inputs) instead "
+                         "of generating them: the process then dispatches no generator kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run plain copies of known size (for HBM counter calibration) and exit")
     ap.add_argument("--summarize-profile", default=None, metavar="DIR",
@@ -196,16 +209,70 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = S.get_config(args.workload)
+    if args.save_inputs:
+        save_inputs(args.save_inputs, S.get_config(args.workload), S, torch, dev)
+        return
+
+    res = bench_forward(args.workload, args, np, torch, moe, S, dev, primary=True)
+    if args.workload == "decode" and not args.no_extra:
+        # the other forward workloads, each timed the same way on its own inputs
+        for name in ("prefill", "skew", "fp8"):
+            torch.cuda.empty_cache()
+            res[name] = bench_forward(name, args, np, torch, moe, S, dev, primary=False)
+    print(json.dumps(res), flush=True)
+
+
+_INPUT_FILES = ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
+
+
+def save_inputs(path, c, S, torch, dev):
+    """The workload's inputs, generated on the GPU, as raw .npy files under path."""
+    import numpy as np
+    os.makedirs(path, exist_ok=True)
+    t = {"x": S.gen_x(c, device=dev), "w_router": S.gen_router(c, device=dev),
+         "bias": S.gen_bias(c, device=dev), **S.gen_experts(c, device=dev)}
+    for k, v in t.items():
+        v = v.cpu()
+        if v.dtype == torch.bfloat16:
+            v = v.view(torch.int16)
+        np.save(os.path.join(path, k + ".npy"), v.numpy())
+    with open(os.path.join(path, "workload.json"), "w") as f:
+        json.dump({"workload": c.name, "T": c.T, "dtypes": {k: str(v.dtype) for k, v in t.items()}},
+                  f)
+    log(f"inputs of {c.name} written to {path}")
+
+
+def load_inputs(path, c, torch, dev):
+    """Inputs written by save_inputs, uploaded with plain host-to-device copies."""
+    import numpy as np
+    meta = json.load(open(os.path.join(path, "workload.json")))
+    assert meta["workload"] == c.name and meta["T"] == c.T, (meta, c.name, c.T)
+    out = {}
+    for k, dt in meta["dtypes"].items():
+        a = torch.from_numpy(np.load(os.path.join(path, k + ".npy")))
+        if dt == "torch.bfloat16":
+            a = a.view(torch.bfloat16)
+        out[k] = a.to(dev)
+    ex = {k: out[k] for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down") if k in out}
+    return out["x"], out["w_router"], out["bias"], ex
+
+
+def bench_forward(name, args, np, torch, moe, S, dev, primary):
+    """Time moe_forward on one workload; returns the JSON line (primary) or its object."""
+    c = S.get_config(name)
     cfg = moe.cfg_from(c)
     T = c.T
     log(f"workload {c.name}: T={T} H={c.hidden} I={c.inter} E={c.n_experts}+{c.n_shared} "
-        f"K={c.topk} w={c.w_dtype}; generating inputs on the GPU")
+        f"K={c.topk} w={c.w_dtype}; " + ("reading inputs" if args.load_inputs and primary
+                                         else "generating inputs on the GPU"))
     t0 = time.time()
-    x = S.gen_x(c, device=dev)
-    wr = S.gen_router(c, device=dev)
-    b = S.gen_bias(c, device=dev)
-    ex = S.gen_experts(c, device=dev)
+    if args.load_inputs and primary:
+        x, wr, b, ex = load_inputs(args.load_inputs, c, torch, dev)
+    else:
+        x = S.gen_x(c, device=dev)
+        wr = S.gen_router(c, device=dev)
+        b = S.gen_bias(c, device=dev)
+        ex = S.gen_experts(c, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     y = torch.empty_like(x)
@@ -234,7 +301,8 @@ def main():
         moe.profile_enable(False)
         kern = moe.profile_read()
         ms = ev0.elapsed_time(ev1) / args.steps
-        log(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {1e3 * (wall1 - wall0) / args.steps:.4f})")
+        log(f"{name}: timed {args.steps} steps: {ms:.4f} ms/step "
+            f"(wall {1e3 * (wall1 - wall0) / args.steps:.4f})")
         for k, (kms, n) in kern.items():
             if n:
                 log(f"  {k:14s} {kms / n * 1e3:9.1f} us/launch  ({n} launches)")
@@ -270,7 +338,10 @@ def main():
         skew = {"steps": args.skew_steps, "gamma": c.gamma,
                 "max_over_mean_load_per_step": [round(v, 3) for v in ratios],
                 "checkpoints": {str(k): {"ms_per_step": round(v[0], 4),
-                                         "tokens_per_s": round(T / (v[0] / 1e3), 1)}
+                                         "tokens_per_s": round(T / (v[0] / 1e3), 1),
+                                         "gemm_gate_up_us": round(
+                                             v[1]["gemm_gate_up"][0] / v[1]["gemm_gate_up"][1] * 1e3, 1),
+                                         "max_over_mean_load": round(ratios[k], 3)}
                                 for k, v in at.items()}}
     else:
         ms_step, kern = timed_forward(x, b)
@@ -306,6 +377,8 @@ def main():
                 "alg_bytes_per_launch": int(gu_bytes), "alg_flops_per_launch": int(gu_flops)}
     if bound == "mfma":
         roofline["mfma_counters"] = measured_mfma(c.name)
+    if c.w_dtype == "e4m3":   # the same kernel against the fp8 matrix cores
+        roofline["mfma_frac_e4m3"] = round(gu_flops / gu_s / 1e12 / MFMA_PEAK_TFLOPS["e4m3"], 4)
     layer = {"ms": round(ms_step, 4), "alg_bytes": int(layer_bytes), "alg_flops": int(layer_flops),
              "hbm_frac": round(layer_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
              "mfma_frac": round(layer_flops / (ms_step / 1e3) / 1e12 /
@@ -314,6 +387,17 @@ def main():
              "kernels_us": {k: round(ms / n * 1e3, 1) for k, (ms, n) in kern.items() if n}}
 
     value = T / (ms_step / 1e3)
+    workload = (f"{c.name}: DeepSeek-V3 MoE layer forward, T={T}, hidden {H}, inter {I}, {E} routed "
+                f"in {c.n_groups} groups (keep {c.topk_groups}) + {Sn} shared, top-{K}, "
+                f"{c.w_dtype} weights")
+    if not primary:
+        obj = {"workload": workload, "T": T, "w_dtype": c.w_dtype, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+               "tokens_per_s": round(value, 1), "roofline": roofline, "layer": layer}
+        if skew is not None:
+            obj["skew"] = skew
+        del x, y, ex, ws, out
+        return obj
     bal = balance_loss_timing(moe, torch, cfg, c, x, wr, ws, dev)
     cpu = None
     if args.cpu_tokens > 0:
@@ -321,7 +405,7 @@ def main():
         if skew is not None:
             cpu["route_update_ms"] = cpu_route_update_ms(c, x, b)
 
-    res = {
+    return {
         "metric": "MoE-layer tokens/s on 1 MI355X; MFMA util (prefill) / HBM GB/s (decode)",
         "value": round(value, 1),
         "unit": "tokens/s",
@@ -334,18 +418,14 @@ def main():
         "vs_baseline": None,
         "dtype": c.w_dtype,
         "data": "synthetic (seeded SplitMix64 inputs, V3 layer shapes)",
-        "config": {"workload": f"{c.name}: DeepSeek-V3 MoE layer forward, T={T}, hidden {H}, "
-                               f"inter {I}, {E} routed in {c.n_groups} groups (keep "
-                               f"{c.topk_groups}) + {Sn} shared, top-{K}, {c.w_dtype} weights",
-                   "T": T, "hidden": H, "inter": I, "n_experts": E, "n_shared": Sn, "topk": K,
-                   "w_dtype": c.w_dtype},
+        "config": {"workload": workload, "T": T, "hidden": H, "inter": I, "n_experts": E,
+                   "n_shared": Sn, "topk": K, "w_dtype": c.w_dtype},
         "roofline": roofline,
         "layer": layer,
         "cpu_baseline": cpu,
         "balance_loss": bal,
         **({"skew": skew} if skew is not None else {}),
     }
-    print(json.dumps(res), flush=True)
 
 
 def bench_backward(args, np, torch, moe, S):

@@ -76,8 +76,12 @@ enum moe_status {
  *   1 <= group_topn <= min(4, n_experts / n_groups), 1 <= topk_groups <= n_groups,
  *   1 <= topk <= min(32, topk_groups * n_experts / n_groups),
  *   n_shared in {0, 1}, hidden % 128 == 0, inter % 128 == 0,
- *   T * (topk + n_shared) < 2^31, T * max(hidden, inter) * sizeof(act) < 2^32,
+ *   hidden * inter * sizeof(w) < 2^32, n_experts * 3 * hidden * 2 < 2^32,
  *   and for E4M3 weights hidden <= 16384, inter <= 16384.
+ * T bounds (else MOE_ERR_SHAPE): T * (topk + n_shared) < 2^31 and
+ *   T * max(hidden, inter) * sizeof(act) < 2^32 (the tiled GEMMs address all
+ *   of x, or one expert's staged rows, with 32-bit byte offsets); at the V3
+ *   shape in bf16 that is T <= 299,593.
  * Dtypes (else MOE_ERR_DTYPE): (act, w) = (F32, F32), (BF16, BF16) or (BF16, E4M3).
  */
 typedef struct moe_cfg {
@@ -247,7 +251,9 @@ int moe_quantize_1x128(const void* x, int64_t rows, int32_t cols, uint8_t* q, fl
                        void* stream);
 
 /*
- * Kernel timing instrumentation (off by default; not thread-safe).
+ * Kernel timing instrumentation (off by default).  The state is per host
+ * thread: moe_profile_enable switches it for the calling thread, whose
+ * compute calls then record, and moe_profile_read reads that thread's record.
  * While enabled, every kernel launch (or, in moe_backward, every stage of
  * launches) of the compute entry points is bracketed by a pair of HIP events
  * on the caller's stream.

@@ -29,10 +29,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIP_FLAGS + ["-x", "hip"] + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,6 +39,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    jobs = []
+    for s in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
+        jobs.append((obj, [hipcc()] + compile_flags + ["-x", "hip", "-c", os.path.join(CSRC, s),
+                                                      "-o", obj]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc()] + HIP_FLAGS + [o for o, _ in jobs] + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -169,9 +169,9 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
   const int c16 = lane & 15, g4 = lane >> 4;
 
   // ---- token rows: buffer resources over the activation codes [T][K]
-  // (gate/up) or the staged rows from the expert's first one (down), and
-  // their scales [rows][K/128]
-  const int a_rows = GATED ? g.T : g.TK + (g.n_exp - g.E) * g.T - row_base;
+  // (gate/up) or this expert's own staged rows (down, at most T), and their
+  // scales [rows][K/128]; the entry points bound T * K below 4 GiB
+  const int a_rows = GATED ? g.T : cnt;
   const __amdgpu_buffer_rsrc_t ars =
       buffer_rsrc(GATED ? g.a : g.a + (size_t)row_base * K, uint32_t(a_rows) * uint32_t(K));
   const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(GATED ? g.as : g.as + (size_t)row_base * KB,

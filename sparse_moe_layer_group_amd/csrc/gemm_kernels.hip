@@ -264,7 +264,7 @@ hipError_t launch_gemm(const GemmArgs<TE>& g, bool gated, int max_mtiles, int ma
   return hipGetLastError();
 }
 
-template hipError_t launch_gemm<bf16_t>(const GemmArgs<bf16_t>&, bool, int, int, hipStream_t);
+// float32 only: bf16 layers take the streaming and tiled GEMMs
 template hipError_t launch_gemm<float>(const GemmArgs<float>&, bool, int, int, hipStream_t);
 
 int gemm_tile_m() { return 64; }

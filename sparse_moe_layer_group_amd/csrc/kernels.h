@@ -72,10 +72,7 @@ struct TileArgs {
   bf16_t* out_g;              // mode 2 (gated, for the backward): G and U too, [rows][N]
   bf16_t* out_u;
 };
-#ifndef MOE_TILE_MBW
-#define MOE_TILE_MBW 5  // 32-row MFMA blocks per wave of the tiled GEMM (2 waves along M)
-#endif
-constexpr int kTileM = 64 * MOE_TILE_MBW;
+constexpr int kTileM = 320;  // token rows per tile of the tiled GEMM (2 waves of 5 x 32 rows)
 hipError_t launch_tile_gemm(const TileArgs& g, int mode, int max_mtiles, hipStream_t st);  // modes as above
 
 int gemm_tile_m();

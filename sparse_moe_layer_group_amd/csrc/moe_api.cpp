@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <cstring>
 #include <vector>
 
@@ -101,11 +102,17 @@ int validate_cfg(const moe_cfg* c) {
   if (!f32 && !bf16 && !fp8) return MOE_ERR_DTYPE;
   // the E4M3 GEMM holds at most 128 weight scales along K per wave
   if (fp8 && (c->hidden > 16384 || c->inter > 16384)) return MOE_ERR_SHAPE;
+  // one expert matrix spans less than 4 GiB (32-bit buffer ranges of the
+  // tiled GEMMs), and so do the router's bf16 weight parts [E][3H]
+  const int64_t wb = int64_t(elem_bytes(c->w_dtype));
+  if (int64_t(c->hidden) * c->inter * wb >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+  if (int64_t(c->n_experts) * 3 * c->hidden * 2 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
-// T bounds: row counts fit int32, and one expert's activation rows (at most T)
-// span less than 4 GiB, the reach of the tiled GEMMs' 32-bit offsets.
+// T bounds: row counts fit int32, and T activation rows (all of x, or one
+// expert's staged rows, at most T) span less than 4 GiB, the reach of the
+// tiled GEMMs' 32-bit buffer ranges and offsets.
 int validate_T(const moe_cfg* c, int64_t T) {
   if (T < 0) return MOE_ERR_SHAPE;
   if (T * int64_t(c->topk + c->n_shared) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
@@ -163,18 +170,30 @@ struct Prof {
     return e;
   }
 };
-Prof g_prof;
+// Instrumentation state is per host thread: calls on distinct workspaces from
+// different threads stay independent with profiling on.  A thread's events
+// are kept for reuse until the process ends.
+thread_local Prof g_prof;
 
 // run one launcher, bracketed by events when instrumentation is on
 template <typename F> hipError_t timed(int slot, hipStream_t st, F&& f) {
   if (!g_prof.on) return f();
   hipEvent_t a = g_prof.get(), b = g_prof.get();
-  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
-  hipEventRecord(a, st);
-  hipError_t err = f();
-  hipEventRecord(b, st);
-  g_prof.recs.push_back({slot, a, b});
-  return err;
+  if (a == nullptr || b == nullptr) {
+    if (a != nullptr) g_prof.pool.push_back(a);
+    if (b != nullptr) g_prof.pool.push_back(b);
+    return hipErrorOutOfMemory;
+  }
+  hipError_t err = hipEventRecord(a, st);
+  if (err == hipSuccess) err = f();
+  hipError_t end = err == hipSuccess ? hipEventRecord(b, st) : err;
+  if (end == hipSuccess) {
+    g_prof.recs.push_back({slot, a, b});
+  } else {
+    g_prof.pool.push_back(a);
+    g_prof.pool.push_back(b);
+  }
+  return err != hipSuccess ? err : end;
 }
 
 #define MOE_TRY(expr)                         \
@@ -273,7 +292,6 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
   const int TK = T * K;
   const int bm = tile_rows(c);
   const int max_mt = (TK + bm - 1) / bm + E + S * ((T + bm - 1) / bm);
-  const bool big = use_big_tiles(c);
   TE* hst = at<TE>(ws, L.hst);
   TE* yst = at<TE>(ws, L.yst);
   const int32_t* chunk_start = at<int32_t>(ws, L.chunk_start);
@@ -299,13 +317,14 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
       hipError_t err = moe::launch_stream_gemm(sa, 1, stream_blocks(I / 64), st);
       if (err != hipSuccess || !tiles) return err;
     }
-    if (big) {
+    if constexpr (std::is_same<TE, bf16_t>::value) {
       moe::TileArgs ta{reinterpret_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w->w_gate),
                        static_cast<const bf16_t*>(w->w_up), reinterpret_cast<bf16_t*>(hst), r.perm,
                        r.counts, r.offsets, mt_start, E, E + S, T, TK, I, H};
       return moe::launch_tile_gemm(ta, 1, max_mt, st);
+    } else {
+      return moe::launch_gemm<TE>(g1, true, max_mt, 4 * cu_count(), st);
     }
-    return moe::launch_gemm<TE>(g1, true, max_mt, 4 * cu_count(), st);
   }));
   moe::GemmArgs<TE> g2{hst, static_cast<const TE*>(w->w_down), nullptr, yst, r.perm, r.counts,
                        r.offsets, mt_start, E, E + S, T, TK, H, I};
@@ -318,13 +337,14 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
       hipError_t err = moe::launch_stream_gemm(sa, 0, stream_blocks(H / 128), st);
       if (err != hipSuccess || !tiles) return err;
     }
-    if (big) {
+    if constexpr (std::is_same<TE, bf16_t>::value) {
       moe::TileArgs ta{reinterpret_cast<const bf16_t*>(hst), static_cast<const bf16_t*>(w->w_down),
                        nullptr, reinterpret_cast<bf16_t*>(yst), r.perm, r.counts, r.offsets,
                        mt_start, E, E + S, T, TK, H, I};
       return moe::launch_tile_gemm(ta, 0, max_mt, st);
+    } else {
+      return moe::launch_gemm<TE>(g2, false, max_mt, 4 * cu_count(), st);
     }
-    return moe::launch_gemm<TE>(g2, false, max_mt, 4 * cu_count(), st);
   }));
   MOE_TRY(timed(K_COMBINE, st, [&] {
     return moe::launch_combine<TE>(yst, r.slot, r.gate, residual, y, T, K, H, TK, S, st);

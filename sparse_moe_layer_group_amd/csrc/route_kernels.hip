@@ -284,77 +284,6 @@ __global__ __launch_bounds__(512, 1) void router_tile_kernel(const bf16_t* __res
     }
 }
 
-// P[ks][t][e] for one K chunk: wave tile 32 tokens x 32 experts (2 x 2 MFMA
-// 16x16x32 tiles), block = 4 waves over 128 experts.  Operands are loaded
-// straight from global memory in MFMA order with the 128-wide step K map of
-// the streaming GEMM (lane l owns k = 32*(l/16) .. +31 of each step).
-__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ wt3,
-                                                          float* __restrict__ P, int T, int H,
-                                                          int E, int kchunk) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 32;
-  const int e0 = blockIdx.y * 128 + wave * 32;
-  const int ks = blockIdx.z;
-  const int kb = ks * kchunk, ke = min(H, kb + kchunk);
-  if (e0 >= E) return;  // whole wave; no barrier in this kernel
-  const int koff = 32 * (lane >> 4);
-  const bf16_t* arow[2];
-  const bf16_t* brow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t = t0 + i * 16 + (lane & 15);
-    arow[i] = (t < T) ? x + (size_t)t * H + koff : nullptr;
-    const int e = e0 + i * 16 + (lane & 15);
-    brow[i] = (e < E) ? wt3 + (size_t)e * 3 * H + koff : nullptr;
-  }
-  const size_t part = (size_t)H;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = kb; k < ke; k += 128) {
-    u32x4 a[2][4], b[3][2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        a[i][q] = arow[i] ? *reinterpret_cast<const u32x4*>(arow[i] + k + q * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          b[p][j][q] = brow[j] ? *reinterpret_cast<const u32x4*>(brow[j] + p * part + k + q * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a[i][q]), __builtin_bit_cast(bf16x8, b[p][j][q]),
-                acc[i][j], 0, 0, 0);
-  }
-  float* Pk = P + (size_t)ks * T * E;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = t0 + i * 16 + 4 * (lane >> 4) + q;
-        const int e = e0 + j * 16 + (lane & 15);
-        if (t < T && e < E) Pk[(size_t)t * E + e] = acc[i][j][q];
-      }
-}
-
 // ============================================================================
 // Node-limited selection, one wave per token.
 //
@@ -719,10 +648,14 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, float* __
 static int router_chunk(int H) { return ((H + 7) / 8 + 127) / 128 * 128; }
 
 // Small batches: the bf16x3 router reading W_r (float32 [H][E]) directly.
-// Same tiling and K map as router_mfma_kernel; each lane loads the 8
-// consecutive k of its expert column as float32 (W_r stride E) and splits
-// them into the hi / mid / lo bfloat16 parts in registers, so no separate
-// split pass runs.
+// P[ks][t][e] for one K chunk: wave tile 32 tokens x 32 experts (2 x 2 MFMA
+// 16x16x32 tiles), block = 4 waves over 128 experts.  Operands are loaded
+// straight from global memory in MFMA order with the 128-wide step K map of
+// the streaming GEMM (lane l owns k = 32*(l/16) .. +31 of each step).  Each
+// lane loads the 8 consecutive k of its expert column as float32 (W_r stride
+// E) and splits them into the hi / mid / lo bfloat16 parts in registers, so
+// no separate split pass runs (a split pass plus the MFMA kernel measured
+// 44 us at 256 tokens, this kernel 26 us).
 __global__ __launch_bounds__(256) void router_fused_kernel(const bf16_t* __restrict__ x,
                                                            const float* __restrict__ wr,
                                                            float* __restrict__ P, int T, int H,
@@ -839,10 +772,7 @@ hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt
   const int chunk = router_chunk(H);
   if (x_bf16) {
     const int tc = router_tile_chunks(T, H, E);
-#ifndef MOE_ROUTER_FUSED
-#define MOE_ROUTER_FUSED 1
-#endif
-    if (tc == 0 && MOE_ROUTER_FUSED) {
+    if (tc == 0) {
       hipLaunchKernelGGL(router_fused_kernel, dim3((T + 31) / 32, (E + 127) / 128, ks), dim3(256),
                          0, st, static_cast<const bf16_t*>(x), wr, P, T, H, E, chunk);
       return hipGetLastError();
@@ -851,16 +781,11 @@ hipError_t launch_router(const void* x, bool x_bf16, const float* wr, bf16_t* wt
                        wr, wt3, H, E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (tc > 0) {
-      const int nsteps = 3 * H / RT_TBK;
-      const int spc = (nsteps + tc - 1) / tc;
-      hipLaunchKernelGGL(router_tile_kernel,
-                         dim3((T + RT_TBM - 1) / RT_TBM, (E + RT_TBN - 1) / RT_TBN, tc), dim3(512),
-                         0, st, static_cast<const bf16_t*>(x), wt3, P, T, H, E, spc);
-      return hipGetLastError();
-    }
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 31) / 32, (E + 127) / 128, ks), dim3(256), 0,
-                       st, static_cast<const bf16_t*>(x), wt3, P, T, H, E, chunk);
+    const int nsteps = 3 * H / RT_TBK;
+    const int spc = (nsteps + tc - 1) / tc;
+    hipLaunchKernelGGL(router_tile_kernel,
+                       dim3((T + RT_TBM - 1) / RT_TBM, (E + RT_TBN - 1) / RT_TBN, tc), dim3(512),
+                       0, st, static_cast<const bf16_t*>(x), wt3, P, T, H, E, spc);
   } else {
     dim3 grid((T + RB_M - 1) / RB_M, (E + RB_N - 1) / RB_N, ks);
     hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, st,

@@ -21,8 +21,7 @@
 // LDS copies of that shape stream about 86 GB/s per CU from L2 against about
 // 63 GB/s for 16 rows of 64 bytes, which made K steps of 64 with two stages
 // (144 KB in all) faster than K steps of 32 with four stages
-// (gate/up at 8192 tokens: 4.89 -> 4.54 ms).  MOE_TILE_K64=0 builds the
-// K-32 form (NSA / NSB stages, copies NS-2 steps ahead).
+// (gate/up at 8192 tokens: 4.89 -> 4.54 ms).
 //
 // Schedule of K step kt (four k16 slices s0..s3):
 //   MFMAs of s0, s1, s2 of kt, each with the next slice's fragment reads
@@ -40,8 +39,8 @@
 // Task order: for each expert and column tile, its row tiles are consecutive
 // workgroups, so the workgroups sharing a weight tile run together and read it
 // from HBM once (L2 / MALL serve the others).  Dealing each XCD a contiguous
-// eighth of the tasks (MOE_TILE_XCD=1) keeps an expert's token rows in one L2
-// but measured no faster.
+// eighth of the tasks keeps an expert's token rows in one L2 but measured 1-2%
+// slower.
 #include <type_traits>
 
 #include "common.h"
@@ -51,30 +50,12 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_TILE_XCD
-#define MOE_TILE_XCD 0
-#endif
-#ifndef MOE_TILE_K64
-#define MOE_TILE_K64 1
-#endif
-#if MOE_TILE_K64
 // K steps of 64: rows of 128 bytes, copied 8 rows per 1 KB copy; two stages
-#undef MOE_TILE_NSA
-#undef MOE_TILE_NSB
-#define MOE_TILE_NSA 2
-#define MOE_TILE_NSB 2
-#endif
-#ifndef MOE_TILE_NSA
-#define MOE_TILE_NSA 4
-#endif
-#ifndef MOE_TILE_NSB
-#define MOE_TILE_NSB 4
-#endif
-constexpr int MBW = MOE_TILE_MBW;            // 32-row MFMA blocks per wave (2 waves along M)
-constexpr int TBM = 64 * MBW, TBN = 256, TBK = MOE_TILE_K64 ? 64 : 32;
+constexpr int MBW = kTileM / 64;             // 32-row MFMA blocks per wave (2 waves along M)
+constexpr int TBM = kTileM, TBN = 256, TBK = 64;
 constexpr int RPC = 1024 / (TBK * 2);        // rows per 1 KB copy
 constexpr int CPR = TBK / 8;                 // 16-byte chunks per row
-constexpr int NSA = MOE_TILE_NSA, NSB = MOE_TILE_NSB;
+constexpr int NSA = 2, NSB = 2;
 constexpr int WN = 4, NWAVE = 2 * WN, NTHREAD = 64 * NWAVE;
 constexpr int NJ = TBN / WN / 32;            // 32-column MFMA blocks per wave
 constexpr int ASTAGE = TBM * TBK, BSTAGE = TBN * TBK;  // bf16 elements per stage
@@ -82,16 +63,11 @@ constexpr int ACP = TBM / RPC / 4;           // 1 KB copies per token-row wave p
 constexpr int BCP = TBN / RPC / 4;           // ... per weight-row wave
 static_assert(TBM == kTileM, "row tile shared with the tile prefix scan");
 static_assert(TBM % 64 == 0 && NJ == 2, "tile configuration");
-static_assert(MOE_TILE_K64 ? (NSA == 2 && NSB == 2) : (NSA >= 3 && NSB >= 3),
-              "copies run at least one step ahead of the barrier");
 static_assert((NSA * ASTAGE + NSB * BSTAGE) * 2 <= 160 * 1024, "LDS per CU");
 static_assert(NSA * ACP < 64 && NSB * BCP < 64, "vmcnt field is 6 bits");
 
-// chunk c of row r sits at c ^ ((r/2) % 4) (rows of 4 chunks) or c ^ (r % 8)
-// (rows of 8 chunks)
-MOE_DEV int swz(int row, int chunk) {
-  return MOE_TILE_K64 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 1) & 3));
-}
+// chunk c of row r sits at c ^ (r % 8)
+MOE_DEV int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
 MOE_DEV bf16x8 ld_frag(const bf16_t* base, int row, int chunk) {
   return *reinterpret_cast<const bf16x8*>(base + row * TBK + (swz(row, chunk) << 3));
@@ -116,19 +92,8 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
   // column tiles (N % 128 == 0; a down tile may be half past N)
   const int n_nt = GATED ? g.N / (TBN / 2) : (g.N + TBN - 1) / TBN;
   const int n_tasks = g.mt_start[g.n_exp] * n_nt;
-#if MOE_TILE_XCD
-  // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-  // b % 8).  XCD x takes the x-th contiguous eighth of the task list, so the
-  // column tiles of one expert run in one XCD and its token rows are fetched
-  // into one L2.
-  const int per = (n_tasks + 7) >> 3;
-  const int j = blockIdx.x >> 3;
-  const int task = (blockIdx.x & 7) * per + j;
-  if (j >= per || task >= n_tasks) return;  // uniform per workgroup, before any barrier
-#else
   const int task = blockIdx.x;
   if (task >= n_tasks) return;  // uniform per workgroup, before any barrier
-#endif
   // task -> expert, then (column tile, row tile) with row tiles fastest
   int lo = 0, hi = g.n_exp - 1;
   while (lo < hi) {
@@ -177,10 +142,10 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
       off[i] = (uint32_t(col) * uint32_t(K) + uint32_t(swz(r, lane % CPR) * 8)) * 2u;
     }
   } else {
-    const int staged_rows = g.TK + (g.n_exp - g.E) * g.T;
+    // gate/up: all of x (T rows); down: this expert's own staged rows (at most
+    // T).  Both spans stay below 4 GiB: the entry points bound T * K * 2.
     crs = GATED ? buffer_rsrc(g.a, uint32_t(g.T) * uint32_t(K) * 2u)
-                : buffer_rsrc(g.a + (size_t)row_base * K,
-                              uint32_t(staged_rows - row_base) * uint32_t(K) * 2u);
+                : buffer_rsrc(g.a + (size_t)row_base * K, uint32_t(cnt) * uint32_t(K) * 2u);
 #pragma unroll
     for (int i = 0; i < ACP; ++i) {
       const int r = RPC * (ACP * cw + i) + lane / CPR;
@@ -202,12 +167,6 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
 #pragma unroll
       for (int i = 0; i < ACP; ++i) copy16_to_lds(crs, off[i] + koff, d + RPC * i * TBK);
     }
-  };
-  // wait until this wave's copies of all but its last n issued steps landed
-  auto wait_copies = [&](auto n_c) {
-    constexpr int n = decltype(n_c)::value;
-    if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm(n * BCP));
-    else __builtin_amdgcn_s_waitcnt(vm_wait_imm(n * ACP));
   };
 
   // ---- wave sub-tile: active 32-row blocks (uniform per wave)
@@ -249,7 +208,6 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
-#if MOE_TILE_K64
     // four k16 slices per step; slice s+1 is read during the MFMAs of slice
     // s.  After the reads of slice 3 of kt: wait for this wave's copies of
     // kt+1 and its LDS reads, barrier (every wave's copies of kt+1 landed and
@@ -293,49 +251,7 @@ __global__ __launch_bounds__(NTHREAD, 1) void tile_gemm_kernel(TileArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no copy left in flight
-#else
-    const int lead = copies_b ? NSB - 1 : NSA - 1;  // steps a wave's copies run ahead
-    for (int p = 0; p < lead; ++p) copy_step(p);
-    // this wave's step 0 landed: its copies of steps 1 .. lead-1 stay in flight
-    if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSB - 2) * BCP));
-    else __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSA - 2) * ACP));
-    __builtin_amdgcn_s_barrier();
-    Frags f0, f1;
-    rd(f0, 0, 0);
-    // instruction order inside a phase: one fragment read after each of the
-    // first MACT+2 MFMAs, then the remaining MFMAs
-    auto interleave = [&]() {
-#pragma unroll
-      for (int k = 0; k < MACT + NJ; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-      if (MACT * NJ > MACT + NJ) __builtin_amdgcn_sched_group_barrier(0x008, MACT * NJ - MACT - NJ, 0);
-    };
-    for (int kt = 0; kt < nk; ++kt) {
-      rd(f1, kt, 1);
-      mma(f0);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-      // this wave's copies of kt+1 landed; after the barrier every wave's
-      // have, and every wave has read its fragments of step kt-1, so the
-      // stages of kt-1 are refilled with step kt-1+NSB (weights) or
-      // kt-1+NSA (token rows).  After the last step the reads of step nk
-      // fetch data that is never used.
-      if (copies_b) __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSB - 3) * BCP));
-      else __builtin_amdgcn_s_waitcnt(vm_wait_imm((NSA - 3) * ACP));
-      __builtin_amdgcn_s_barrier();
-      copy_step(kt + lead);
-      __builtin_amdgcn_sched_barrier(0);
-      rd(f0, kt + 1, 0);
-      mma(f1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no copy left in flight
-#endif
   };
-  (void)wait_copies;
   static_assert(MBW <= 5, "dispatch below covers up to 5 blocks");
   switch (mact) {
     case 5: mainloop(std::integral_constant<int, (MBW >= 5 ? 5 : 0)>{}); break;

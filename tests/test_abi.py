@@ -216,3 +216,47 @@ def test_backward_argument_checks():
                           one, one, one, one, ctypes.c_size_t(100), None) == -4
     assert L.moe_backward(ctypes.byref(c), 0, None, None, None, None, None, None, None, None,
                           None, None, None, ctypes.c_size_t(0), None) == 0
+
+
+def _largest_accepted_T(c, hi=1 << 22):
+    lo = 0                                   # moe_workspace_bytes(c, lo) > 0 holds for lo = 1
+    lo, hi = 1, hi
+    while lo + 1 < hi:
+        mid = (lo + hi) // 2
+        if moe.workspace_bytes(c, mid) > 0:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+@pytest.mark.parametrize("kw,act_bytes", [(dict(), 2), (dict(w_dtype=moe.E4M3), 2),
+                                          (dict(hidden=1024, inter=4096), 2),
+                                          (dict(act_dtype=moe.F32, w_dtype=moe.F32, hidden=256,
+                                                inter=128, n_experts=16, n_groups=4,
+                                                topk_groups=2, topk=4), 4)])
+def test_accepted_T_keeps_every_32_bit_buffer_range(kw, act_bytes):
+    """At the largest T the library accepts, the byte spans that the tiled
+    GEMMs address with 32-bit offsets stay below 4 GiB: all of x (gate/up,
+    T rows), one expert's staged rows (down: at most T rows, of inter for H
+    and hidden for Y), and one expert's weight matrix; one more token is
+    rejected."""
+    c = _v3(**kw)
+    T = _largest_accepted_T(c)
+    assert moe.workspace_bytes(c, T + 1) == 0
+    H, I = c.hidden, c.inter
+    assert T * H * act_bytes < 2 ** 32          # x rows of the gate/up GEMMs
+    assert T * I * act_bytes < 2 ** 32          # one expert's staged H rows (down GEMM)
+    assert T * (c.topk + c.n_shared) < 2 ** 31  # row counts and offsets in int32
+    wb = {moe.F32: 4, moe.BF16: 2, moe.E4M3: 1}[c.w_dtype]
+    assert H * I * wb < 2 ** 32
+    if not kw:
+        assert T == 299593                      # V3 in bf16: 299,593 * 7168 * 2 < 2^32
+
+
+def test_weight_matrix_over_4_GiB_is_rejected():
+    # hidden * inter * 2 bytes >= 2^32: one expert matrix beyond the 32-bit ranges
+    assert moe.workspace_bytes(_v3(hidden=65536, inter=32768, n_experts=8, n_groups=8,
+                                   topk_groups=8, topk=8, group_topn=1), 16) == 0
+    assert moe.workspace_bytes(_v3(hidden=65536, inter=16384, n_experts=8, n_groups=8,
+                                   topk_groups=8, topk=8, group_topn=1), 16) > 0
