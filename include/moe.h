@@ -65,7 +65,9 @@ enum moe_status {
   MOE_ERR_DTYPE = -3,      /* unsupported dtype combination */
   MOE_ERR_WORKSPACE = -4,  /* workspace NULL or smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = -5,        /* a HIP runtime call or kernel launch failed */
-  MOE_ERR_DEVICE = -6      /* the current device is not a gfx950 GPU */
+  MOE_ERR_DEVICE = -6,     /* the current device is not a gfx950 GPU */
+  MOE_ERR_TOO_LARGE = -7   /* moe_forward_noalloc: the batch needs more than
+                              MOE_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /*
@@ -167,6 +169,27 @@ int moe_route(const moe_cfg* cfg, int64_t T, const void* x, const float* w_route
 int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
                 const float* bias, const moe_experts* w, const void* residual, void* y,
                 const moe_routing* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results as moe_forward, with no workspace argument.
+ * Its scratch is a static device buffer of MOE_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on every GPU it runs on until the process ends; the
+ * call allocates nothing (no hipMalloc, no library allocation, no timing
+ * events: moe_profile_* do not record it).
+ *   Arguments as in moe_forward.  A batch whose moe_workspace_bytes(cfg, T)
+ *   exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_TOO_LARGE without
+ *   launching (at the V3 shape: T <= 321 in bf16, T <= 342 with E4M3 weights).
+ * Every call on one GPU uses that GPU's one buffer: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be ordered by the
+ * caller.  The buffer keeps the last call's contents; no result depends on
+ * them (every scratch byte a call reads, it has written earlier in the call).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+                        const float* bias, const moe_experts* w, const void* residual, void* y,
+                        const moe_routing* out, void* stream);
 
 /*
  * Loss-free bias step on the loads of one batch.

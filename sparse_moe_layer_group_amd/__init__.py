@@ -18,6 +18,7 @@ import torch
 
 __all__ = ["F32", "BF16", "E4M3", "MoeError", "lib", "lib_path", "make_cfg", "cfg_from",
            "workspace_bytes", "alloc_workspace", "alloc_routing", "route", "forward",
+           "forward_noalloc", "NOALLOC_SCRATCH_BYTES",
            "bias_update", "quantize_1x128", "balance_loss", "backward", "backward_workspace_bytes",
            "alloc_backward_workspace", "profile_enable", "profile_read",
            "status_string", "abi_version", "EXPORTED_SYMBOLS"]
@@ -29,7 +30,9 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, E4M3: torch.uint8}
 EXPORTED_SYMBOLS = ("moe_workspace_bytes", "moe_route", "moe_forward", "moe_bias_update",
                     "moe_profile_enable", "moe_profile_read", "moe_profile_kernel_name",
                     "moe_status_string", "moe_abi_version", "moe_quantize_1x128",
-                    "moe_balance_loss", "moe_backward", "moe_backward_workspace_bytes")
+                    "moe_balance_loss", "moe_backward", "moe_backward_workspace_bytes",
+                    "moe_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20    # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -80,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [ctypes.POINTER(_Cfg), I64, P, P, P, ctypes.POINTER(_Experts), P, P,
                                   ctypes.POINTER(_Routing), P, SZ, P]
         L.moe_forward.restype = I32
+        L.moe_forward_noalloc.argtypes = [ctypes.POINTER(_Cfg), I64, P, P, P,
+                                          ctypes.POINTER(_Experts), P, P, ctypes.POINTER(_Routing),
+                                          P]
+        L.moe_forward_noalloc.restype = I32
         L.moe_bias_update.argtypes = [ctypes.POINTER(_Cfg), I64, P, P, ctypes.c_float, P]
         L.moe_bias_update.restype = I32
         L.moe_status_string.argtypes = [I32]
@@ -228,11 +235,8 @@ def route(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor
         raise MoeError(rc, "moe_route")
 
 
-def forward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
-            experts: Dict[str, torch.Tensor], y: torch.Tensor, ws: torch.Tensor,
-            residual: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None,
-            stream=None) -> None:
-    """moe_forward: the whole layer into ``y`` (routing into ``out`` when given)."""
+def _forward_args(cfg: _Cfg, x, w_router, bias, experts, y, residual, out):
+    """Checked pointer arguments shared by moe_forward and moe_forward_noalloc."""
     T = x.shape[0]
     H, I, n = cfg.hidden, cfg.inter, cfg.n_experts + cfg.n_shared
     adt, wdt = _TORCH_DT[cfg.act_dtype], _TORCH_DT[cfg.w_dtype]
@@ -252,12 +256,34 @@ def forward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tens
     ex = _Experts(*[experts[k].data_ptr() if experts.get(k) is not None else None
                     for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")])
     r = _routing_struct(cfg, T, out) if out is not None else None
-    rc = lib().moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(bias),
+    return ex, r
+
+
+def forward(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+            experts: Dict[str, torch.Tensor], y: torch.Tensor, ws: torch.Tensor,
+            residual: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None,
+            stream=None) -> None:
+    """moe_forward: the whole layer into ``y`` (routing into ``out`` when given)."""
+    ex, r = _forward_args(cfg, x, w_router, bias, experts, y, residual, out)
+    rc = lib().moe_forward(ctypes.byref(cfg), x.shape[0], _ptr(x), _ptr(w_router), _ptr(bias),
                            ctypes.byref(ex), _ptr(residual), _ptr(y),
                            ctypes.byref(r) if r is not None else None, _ptr(ws),
                            ws.numel() if ws is not None else 0, _stream(stream))
     if rc != 0:
         raise MoeError(rc, "moe_forward")
+
+
+def forward_noalloc(cfg: _Cfg, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+                    experts: Dict[str, torch.Tensor], y: torch.Tensor,
+                    residual: Optional[torch.Tensor] = None,
+                    out: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> None:
+    """moe_forward_noalloc: moe_forward with the library's static device scratch (no workspace)."""
+    ex, r = _forward_args(cfg, x, w_router, bias, experts, y, residual, out)
+    rc = lib().moe_forward_noalloc(ctypes.byref(cfg), x.shape[0], _ptr(x), _ptr(w_router),
+                                   _ptr(bias), ctypes.byref(ex), _ptr(residual), _ptr(y),
+                                   ctypes.byref(r) if r is not None else None, _stream(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_forward_noalloc")
 
 
 def backward_workspace_bytes(cfg: _Cfg, T: int) -> int:

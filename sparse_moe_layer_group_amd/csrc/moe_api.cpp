@@ -712,6 +712,34 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+
+// Device scratch of moe_forward_noalloc: a file-scope array that every GPU the
+// library runs on holds once, from code-object load until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol): it passes the device address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[64];
+
+// this device's address of the scratch array (looked up on its first use)
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // concurrent first calls look up the same address; any of them may store it
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -760,6 +788,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case MOE_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case MOE_ERR_TOO_LARGE:
+      return "batch needs more scratch than moe_forward_noalloc's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -816,6 +846,25 @@ int moe_forward(const moe_cfg* cfg, int64_t T, const void* x, const float* w_rou
   return run_experts<float>(*cfg, int(T), static_cast<const float*>(x), w,
                             static_cast<const float*>(residual), static_cast<float*>(y), r, ws, L,
                             st);
+}
+
+int moe_forward_noalloc(const moe_cfg* cfg, int64_t T, const void* x, const float* w_router,
+                        const float* bias, const moe_experts* w, const void* residual, void* y,
+                        const moe_routing* out, void* stream) {
+  int rc = validate_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = validate_T(cfg, T)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (make_layout(*cfg, T).total > kScratchBytes) return MOE_ERR_TOO_LARGE;
+  if ((rc = check_device()) != MOE_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws)) != MOE_OK) return rc;
+  // no timing events for this entry point: creating them would allocate
+  const bool prof = g_prof.on;
+  g_prof.on = false;
+  rc = moe_forward(cfg, T, x, w_router, bias, w, residual, y, out, ws, kScratchBytes, stream);
+  g_prof.on = prof;
+  return rc;
 }
 
 size_t moe_backward_workspace_bytes(const moe_cfg* cfg, int64_t T) {
