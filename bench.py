@@ -46,8 +46,10 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
-    "decode": {"src_sha256": "4a4e21a09259d43cdd3d4ecfb2c414c80c9a5011bc8473fa60e8c3652ae2eef3",
-             "fetch_kib": 8155177.8, "write_kib": 9216.0},
+    "decode": {"src_sha256": "5851aa178b2143b2af5a9c5b5a65bc21ed150f13e7758613b0d98bbef39241e6",
+             "fetch_kib": 8152229.7, "write_kib": 9216.0},
+    "fp8": {"src_sha256": "414ae1717fa3b22e9cd9ca42fbbe792bfa816b3a9f1a619d6a72b43b595484d8",
+            "fetch_kib": 4961546.6, "write_kib": 92203.6},
     "prefill": {"src_sha256": "d25fe2c24e864f3934ea59142c945a682c000c538d8bda9bd03bde984c3eb695",
               "fetch_kib": 12205459.8, "write_kib": 294912.0},
     "backward_prefill_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
