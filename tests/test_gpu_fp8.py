@@ -5,9 +5,9 @@ Page "02 · DeepSeek-V3", §2.2: E4M3 weights with one float32 scale per
 accumulation.  Bars:
   - the 1x128 activation quantiser: codes and scales bit-exact (the oracle
     decides each code from the same float32 quotient);
-  - at the V3 shape (T=4096, 0.1% outliers x50), layer output within 6e-2
-    (max row-relative error) of the oracle on the dequantised weights with
-    unquantised activations;
+  - at the V3 shape (T=4096, 0.1% outliers x50), every row of the layer
+    output within 6e-2 (max row-relative error) of the oracle's E4M3 layer
+    (tests/test_gpu_v3_full.py);
   - layer output against the oracle's emulation, which quantises x and the
     SwiGLU output H the same way but computes in exact arithmetic: within 1e-2
     on inputs whose fp8 products the matrix cores sum exactly (codes of x,
@@ -171,29 +171,7 @@ def test_fp8_forward_is_deterministic():
     assert torch.equal(y0, y1)
 
 
-def test_v3_fp8_routing_and_sampled_output():
-    c = S.get_config("fp8")
-    say(f"V3 fp8: generating inputs on the GPU (T={c.T})")
-    gi = GpuInputs(c)
-    y, out = gi.run_forward()
-    x_cpu = S.gen_x(c, device="cpu")
-    b = S.gen_bias(c, "cpu").numpy()
-    L, s, r, p = oracle_route(c, x_cpu, b)
-    check_routing(c, out, r, "V3 fp8")
-    busiest = int(np.argmax(p.counts))
-    tok_busy = int(p.perm[p.offsets[busiest]])
-    tokens = sorted(set([0, 1, c.T // 2, c.T - 1, tok_busy]))
-    tokens = [t for t in tokens if not r.flagged[t]]
-    yn = y[tokens].float().cpu().numpy()
-    err = row_errors(yn, _oracle(c, tokens=tokens, x_cpu=x_cpu, b=b).y)
-    emu = row_errors(yn, _oracle(c, tokens=tokens, x_cpu=x_cpu, b=b, emulate=True).y)
-    say(f"V3 fp8 sampled tokens {tokens}: vs dequantised weights {np.round(err, 4).tolist()}, "
-        f"vs emulation {np.round(emu, 5).tolist()} (flagged near-ties {int(r.flagged.sum())})")
-    assert err.max() <= OUT_TOL["e4m3"]
-    assert emu.max() <= EMU_TOL
-    del gi, y, out
-    gc.collect()
-    torch.cuda.empty_cache()
+# The V3-shape fp8 batch (T=4096) is compared over every row in test_gpu_v3_full.py.
 
 
 @pytest.mark.parametrize("kw", [dict(T=300, hidden=1152, inter=384), dict(T=200, topk=1, n_shared=0)])
