@@ -50,8 +50,8 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
              "fetch_kib": 8152229.7, "write_kib": 9216.0},
     "fp8": {"src_sha256": "414ae1717fa3b22e9cd9ca42fbbe792bfa816b3a9f1a619d6a72b43b595484d8",
             "fetch_kib": 4961546.6, "write_kib": 92203.6},
-    "prefill": {"src_sha256": "d25fe2c24e864f3934ea59142c945a682c000c538d8bda9bd03bde984c3eb695",
-              "fetch_kib": 12205459.8, "write_kib": 294912.0},
+    "prefill": {"src_sha256": "d126ba0b0c9a91f2987070f4d6c384ffd6c20b9aed7e86ac42a42bfcdd1e0e3b",
+              "fetch_kib": 12190886.6, "write_kib": 294912.0},
     "backward_prefill_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
                             "fetch_kib": 6394862.8, "write_kib": 44214735.7},
     "backward_decode_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
@@ -61,8 +61,8 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "d25fe2c24e864f3934ea59142c945a682c000c538d8bda9bd03bde984c3eb695",
-                "busy": 0.577, "clock_ghz": 1.53, "executed_bf16_tflop": 4.56},
+    "prefill": {"src_sha256": "d126ba0b0c9a91f2987070f4d6c384ffd6c20b9aed7e86ac42a42bfcdd1e0e3b",
+                "busy": 0.578, "clock_ghz": 1.53, "executed_bf16_tflop": 4.56},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
@@ -155,6 +155,27 @@ def summarize_profile(path):
                 k, kid, cn = key
                 print(f"{k[:40]:40s} {kid:6d} {first[key]:9d} {cn:12s} {len(v):10d} "
                       f"{sum(v) / len(v):14.1f} {min(v):14.1f} {max(v):14.1f}")
+            # MFMA utilisation per kernel when the run collected these counters:
+            # busy = MFMA busy SIMD-cycles / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)
+            per = collections.defaultdict(lambda: collections.defaultdict(list))
+            dur = collections.defaultdict(list)
+            for r in rows:
+                kk = (r["Kernel_Name"], int(r["Kernel_Id"]))
+                per[kk][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    dur[kk].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+            need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+            table = [(kk, c) for kk, c in per.items() if all(n in c for n in need) and dur[kk]]
+            if table:
+                print(f"{'kernel':40s} {'id':>6s} {'us':>9s} {'clock GHz':>10s} {'MFMA busy':>10s} "
+                      f"{'bf16 TFLOP':>11s} {'TFLOP/s':>9s}")
+                for (k, kid), c in table:
+                    t = sum(dur[(k, kid)]) / len(dur[(k, kid)])
+                    grbm = sum(c[need[0]]) / len(c[need[0]])
+                    busy = sum(c[need[1]]) / len(c[need[1]]) / (grbm / 8 * 1024)
+                    tf = sum(c[need[2]]) / len(c[need[2]]) * 512 / 1e12
+                    print(f"{k[:40]:40s} {kid:6d} {t * 1e6:9.1f} {grbm / 8 / t / 1e9:10.2f} "
+                          f"{100 * busy:9.1f}% {tf:11.3f} {tf / t:9.1f}")
 
 
 def main():
