@@ -56,6 +56,7 @@ constexpr int kMaxStreamExperts = 1024;  // n_exp bound of the streaming GEMM's 
 // mode 0: out = A W0^T; 1: out = SiLU(x W0^T) * (x W1^T), x rows gathered
 // through perm; 2: as 1, and the two products also to out_g and out_u
 hipError_t launch_stream_gemm(const StreamArgs& g, int mode, int n_blocks, hipStream_t st);
+int stream_waves_per_block(int mode);  // waves of one workgroup of launch_stream_gemm
 
 // LDS-tiled GEMM for experts with many rows (tile_gemm.hip), bf16 only;
 // kTileM-row tiles, gate/up column tiles of 128, down column tiles of 256

@@ -299,12 +299,13 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
   const int smax = stream_max_rows(c, T);
   const bool streams = smax >= 0;
   const bool tiles = smax < T;  // an expert (or the shared one) can have up to T rows
-  // persistent grid of the streaming GEMM: one 4-wave workgroup per CU, fewer
-  // when the largest task count the routing can produce is smaller
-  auto stream_blocks = [&](int n_slices) {
+  // persistent grid of the streaming GEMM: one workgroup per CU, fewer when
+  // the largest task count the routing can produce is smaller
+  auto stream_blocks = [&](int n_slices, int mode) {
     const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
     const long long waves = chunks * n_slices;
-    return int(std::max<long long>(1, std::min<long long>((waves + 3) / 4, (long long)cu_count())));
+    const int wpb = moe::stream_waves_per_block(mode);
+    return int(std::max<long long>(1, std::min<long long>((waves + wpb - 1) / wpb, (long long)cu_count())));
   };
   moe::GemmArgs<TE> g1{x, static_cast<const TE*>(w->w_gate), static_cast<const TE*>(w->w_up), hst,
                        r.perm, r.counts, r.offsets, mt_start, E, E + S, T, TK, I, H};
@@ -314,7 +315,7 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
                          static_cast<const bf16_t*>(w->w_gate), static_cast<const bf16_t*>(w->w_up),
                          reinterpret_cast<bf16_t*>(hst), r.perm, r.counts, r.offsets, chunk_start,
                          E, E + S, T, TK, I, H};
-      hipError_t err = moe::launch_stream_gemm(sa, 1, stream_blocks(I / 64), st);
+      hipError_t err = moe::launch_stream_gemm(sa, 1, stream_blocks(I / 64, 1), st);
       if (err != hipSuccess || !tiles) return err;
     }
     if constexpr (std::is_same<TE, bf16_t>::value) {
@@ -334,7 +335,7 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
                          static_cast<const bf16_t*>(w->w_down), nullptr,
                          reinterpret_cast<bf16_t*>(yst), r.perm, r.counts, r.offsets, chunk_start,
                          E, E + S, T, TK, H, I};
-      hipError_t err = moe::launch_stream_gemm(sa, 0, stream_blocks(H / 128), st);
+      hipError_t err = moe::launch_stream_gemm(sa, 0, stream_blocks(H / 128, 0), st);
       if (err != hipSuccess || !tiles) return err;
     }
     if constexpr (std::is_same<TE, bf16_t>::value) {
@@ -497,8 +498,9 @@ int run_gate_up_keep(const moe_cfg& c, int T, const bf16_t* x, const bf16_t* wg,
   if (streams) {
     const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
     const long long waves = chunks * (I / 64);
+    const int wpb = moe::stream_waves_per_block(2);
     const int blocks =
-        int(std::max<long long>(1, std::min<long long>((waves + 3) / 4, (long long)cu_count())));
+        int(std::max<long long>(1, std::min<long long>((waves + wpb - 1) / wpb, (long long)cu_count())));
     moe::StreamArgs sa{x, wg, wu, h, r.perm, r.counts, r.offsets, at<int32_t>(ws, L.chunk_start),
                        E, E + S, T, TK, I, H, gst, ust};
     hipError_t err = moe::launch_stream_gemm(sa, 2, blocks, st);

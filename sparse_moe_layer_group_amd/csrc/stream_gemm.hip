@@ -6,12 +6,14 @@
 //
 // Work unit = one wave: (expert, column slice, chunk of up to 16 rows).  The
 // wave streams the 128 weight rows of its slice over the whole K range straight
-// from HBM into MFMA operand registers (no LDS), one 64-wide K step (16 KB) at
-// a time, and multiplies them with its token rows gathered from L2 (each token
-// row is fetched once per 128 weight rows).  One 4-wave workgroup per CU:
-// about 64 KB in flight per CU streams HBM fastest on MI355X; deeper pipelines
-// or more waves per CU measured slower (the extra outstanding lines contend in
-// L2).
+// from HBM into MFMA operand registers (no LDS), one 128-wide K step (32 KB,
+// 256 contiguous bytes of each row) at a time, and multiplies them with its
+// token rows gathered from L2 (each token row is fetched once per 128 weight
+// rows).  One workgroup per CU: two waves for gate/up (64 KB in flight per
+// CU), four for down (128 KB).  Measured at 256 tokens, in A/B runs on one
+// box: K steps of 64 with four waves for both took gate/up 2578 / down 1344
+// us, this form 2564 / 1317 us; three or four gate/up waves, K steps of 64
+// with two, or eight down waves were slower.
 //
 // Balanced persistent grid: all tasks cost the same, so with n tasks and S
 // wave slots the kernel runs k = ceil(n/S) rounds on W = ceil(n/k) waves
@@ -19,9 +21,9 @@
 // task of the others.  Dealing n tasks over all S slots instead would leave a
 // partial last round whose duration is that of a full one.
 //
-// K order inside a 64-wide step: lane l owns the 16 consecutive k starting at
-// 16*(l/16) and feeds its 16-byte chunk q (k = 16*(l/16) + 8q .. +7) to the
-// q-th of two 16x16x32 MFMAs.  A and B use the same map, so every product
+// K order inside a 128-wide step: lane l owns the 32 consecutive k starting at
+// 32*(l/16) and feeds its 16-byte chunk q (k = 32*(l/16) + 8q .. +7) to the
+// q-th of four 16x16x32 MFMAs.  A and B use the same map, so every product
 // pairs equal k.  Steps start at a task-dependent rotation of K so that
 // concurrent waves do not all read the same column offset of their rows.
 //
@@ -37,7 +39,9 @@ namespace moe {
 
 namespace {
 
-constexpr int SK = 64;  // K per step
+constexpr int SK = 128;  // K per step
+constexpr int QC = SK / 32;  // 16-byte chunks per lane, row and step
+
 constexpr int NT = 8;   // 16-row weight tiles per wave
 
 MOE_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -45,19 +49,19 @@ MOE_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 // Every lane loads unconditionally (rows past the expert's count read a valid
 // row of the chunk and their outputs are never stored), so the compiler can
 // count outstanding loads exactly.
-MOE_DEV void load_step(u32x4 (&b)[NT][2], u32x4 (&a)[2], const bf16_t* const (&brow)[NT],
+MOE_DEV void load_step(u32x4 (&b)[NT][QC], u32x4 (&a)[QC], const bf16_t* const (&brow)[NT],
                        const bf16_t* arow, int koff) {
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) b[j][q] = *reinterpret_cast<const u32x4*>(brow[j] + koff + q * 8);
+    for (int q = 0; q < QC; ++q) b[j][q] = *reinterpret_cast<const u32x4*>(brow[j] + koff + q * 8);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) a[q] = *reinterpret_cast<const u32x4*>(arow + koff + q * 8);
+  for (int q = 0; q < QC; ++q) a[q] = *reinterpret_cast<const u32x4*>(arow + koff + q * 8);
 }
 
-MOE_DEV void mma_step(f32x4 (&acc)[NT], const u32x4 (&b)[NT][2], const u32x4 (&a)[2]) {
+MOE_DEV void mma_step(f32x4 (&acc)[NT], const u32x4 (&b)[NT][QC], const u32x4 (&a)[QC]) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < QC; ++q)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[q]), as_bf16x8(b[j][q]), acc[j],
@@ -90,12 +94,13 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
   const int n_slices = g.N / cols;
   const int n_tasks = cs_s[g.n_exp] * n_slices;
   const int nsteps = g.K / SK;
-  const int koff0 = 16 * (lane >> 4);
+  const int koff0 = (SK / 4) * (lane >> 4);
 
-  const int slots = gridDim.x * 4;
+  const int wpb = blockDim.x >> 6;
+  const int slots = gridDim.x * wpb;
   const int rounds = (n_tasks + slots - 1) / slots;
   const int active = rounds > 0 ? (n_tasks + rounds - 1) / rounds : 0;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wid = blockIdx.x * wpb + (threadIdx.x >> 6);
   if (wid >= active) return;  // no barriers below
 
   auto decode = [&](int task) {
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int rot = (task * 7) % nsteps;
-    u32x4 b[NT][2], a[2];
+    u32x4 b[NT][QC], a[QC];
     for (int s = 0; s < nsteps; ++s) {
       const int k = rot + s;
       load_step(b, a, brow, arow, (k >= nsteps ? k - nsteps : k) * SK);
@@ -207,12 +212,15 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
   }
 }
 
+int stream_waves_per_block(int mode) { return mode == 0 ? 4 : 2; }
+
 hipError_t launch_stream_gemm(const StreamArgs& g, int mode, int n_blocks, hipStream_t st) {
   if (g.n_exp > kMaxStreamExperts) return hipErrorInvalidValue;
   if (mode == 2 && (g.out_g == nullptr || g.out_u == nullptr)) return hipErrorInvalidValue;
-  if (mode == 1) hipLaunchKernelGGL(stream_gemm_kernel<1>, dim3(n_blocks), dim3(256), 0, st, g);
-  else if (mode == 2) hipLaunchKernelGGL(stream_gemm_kernel<2>, dim3(n_blocks), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL(stream_gemm_kernel<0>, dim3(n_blocks), dim3(256), 0, st, g);
+  const dim3 block(64 * stream_waves_per_block(mode));
+  if (mode == 1) hipLaunchKernelGGL(stream_gemm_kernel<1>, dim3(n_blocks), block, 0, st, g);
+  else if (mode == 2) hipLaunchKernelGGL(stream_gemm_kernel<2>, dim3(n_blocks), block, 0, st, g);
+  else hipLaunchKernelGGL(stream_gemm_kernel<0>, dim3(n_blocks), block, 0, st, g);
   return hipGetLastError();
 }
 
