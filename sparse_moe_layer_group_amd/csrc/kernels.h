@@ -47,12 +47,13 @@ struct StreamArgs {
   const int32_t* perm;
   const int32_t* counts;
   const int32_t* offsets;
-  const int32_t* chunk_start; // [E+S+1] prefix of 16-row chunks of streamed experts
+  const int32_t* chunk_start; // [E+S+1] prefix of kStreamChunk-row chunks of streamed experts
   int E, n_exp, T, TK, N, K;
   bf16_t* out_g;              // mode 2 (gated, for the backward): G and U too, [rows][N]
   bf16_t* out_u;
 };
 constexpr int kMaxStreamExperts = 1024;  // n_exp bound of the streaming GEMM's LDS tables
+constexpr int kStreamChunk = 64;         // token rows per task of the streaming GEMM
 // mode 0: out = A W0^T; 1: out = SiLU(x W0^T) * (x W1^T), x rows gathered
 // through perm; 2: as 1, and the two products also to out_g and out_u
 hipError_t launch_stream_gemm(const StreamArgs& g, int mode, int n_blocks, hipStream_t st);

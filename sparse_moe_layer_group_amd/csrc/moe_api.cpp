@@ -302,7 +302,8 @@ int run_experts(const moe_cfg& c, int T, const TE* x, const moe_experts* w, cons
   // persistent grid of the streaming GEMM: one workgroup per CU, fewer when
   // the largest task count the routing can produce is smaller
   auto stream_blocks = [&](int n_slices, int mode) {
-    const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
+    const long long chunks = (TK + moe::kStreamChunk - 1) / moe::kStreamChunk + E +
+                           (long long)S * ((T + moe::kStreamChunk - 1) / moe::kStreamChunk);
     const long long waves = chunks * n_slices;
     const int wpb = moe::stream_waves_per_block(mode);
     return int(std::max<long long>(1, std::min<long long>((waves + wpb - 1) / wpb, (long long)cu_count())));
@@ -496,7 +497,8 @@ int run_gate_up_keep(const moe_cfg& c, int T, const bf16_t* x, const bf16_t* wg,
   const int smax = stream_max_rows(c, T);
   const bool streams = smax >= 0, tiles = smax < T;
   if (streams) {
-    const long long chunks = (TK + 15) / 16 + E + (long long)S * ((T + 15) / 16);
+    const long long chunks = (TK + moe::kStreamChunk - 1) / moe::kStreamChunk + E +
+                           (long long)S * ((T + moe::kStreamChunk - 1) / moe::kStreamChunk);
     const long long waves = chunks * (I / 64);
     const int wpb = moe::stream_waves_per_block(2);
     const int blocks =

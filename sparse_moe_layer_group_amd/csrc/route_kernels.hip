@@ -511,7 +511,7 @@ MOE_DEV int block_exclusive_scan(int v, int* wave_tot /* LDS [16] */, int* total
 
 // Work tables of the expert GEMMs over E routed experts then S shared experts
 // (T rows each), both with E+S+1 entries:
-//   chunk_start: prefix of ceil(rows/16) over experts with rows <= stream_max
+//   chunk_start: prefix of ceil(rows/kStreamChunk) over experts with rows <= stream_max
 //                (served by the weight-streaming GEMM);
 //   mt_start:    prefix of ceil(rows/bm) over the other experts (tiled GEMM).
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int nchunks,
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const bool str = rows <= stream_max;
   int tot;
   const int off = block_exclusive_scan(e < E ? cnt : 0, wave_tot, &tot);
-  const int sa = block_exclusive_scan(str ? (rows + 15) / 16 : 0, wave_tot, &tot);
+  const int sa = block_exclusive_scan(str ? (rows + kStreamChunk - 1) / kStreamChunk : 0, wave_tot, &tot);
   const int sb = block_exclusive_scan(str ? 0 : (rows + bm - 1) / bm, wave_tot, &tot);
   if (e < E) {
     counts[e] = cnt;
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   const bool str = rows <= stream_max;
   int tot;
   const int off = block_exclusive_scan(e < E ? cnt : 0, wave_tot, &tot);
-  const int sa = block_exclusive_scan(str ? (rows + 15) / 16 : 0, wave_tot, &tot);
+  const int sa = block_exclusive_scan(str ? (rows + kStreamChunk - 1) / kStreamChunk : 0, wave_tot, &tot);
   const int sb = block_exclusive_scan(str ? 0 : (rows + bm - 1) / bm, wave_tot, &tot);
   if (e < E) {
     counts[e] = cnt;

@@ -4,16 +4,20 @@
 // experts) and §5.1 (a decode expert sees few tokens, so its cost is reading
 // its weights from memory, not arithmetic).
 //
-// Work unit = one wave: (expert, column slice, chunk of up to 16 rows).  The
+// Work unit = one wave: (expert, column slice, chunk of up to 64 rows).  The
 // wave streams the 128 weight rows of its slice over the whole K range straight
 // from HBM into MFMA operand registers (no LDS), one 128-wide K step (32 KB,
-// 256 contiguous bytes of each row) at a time, and multiplies them with its
-// token rows gathered from L2 (each token row is fetched once per 128 weight
-// rows).  One workgroup per CU: two waves for gate/up (64 KB in flight per
-// CU), four for down (128 KB).  Measured at 256 tokens, in A/B runs on one
-// box: K steps of 64 with four waves for both took gate/up 2578 / down 1344
-// us, this form 2564 / 1317 us; three or four gate/up waves, K steps of 64
-// with two, or eight down waves were slower.
+// 256 contiguous bytes of each row) at a time, and multiplies them with the
+// chunk's token rows gathered from L2, one to four 16-row tiles, so each
+// weight fragment feeds up to four MFMAs.  (With 16-row chunks the shared
+// expert's 256 decode rows made 16 tasks per slice that each streamed the
+// slice again; at 256 tokens, timing with the shared expert cut to one chunk
+// showed those 15 extra passes cost 98 us of gate/up and 39 us of down.)  One
+// workgroup per CU: two waves for gate/up (64 KB in flight per CU), four for
+// down (128 KB).  Measured at 256 tokens, in A/B runs on one box: K steps of
+// 64 with four waves for both took gate/up 2578 / down 1344 us, 128-wide
+// steps with these wave counts 2564 / 1317 us; three or four gate/up waves,
+// K steps of 64 with two, or eight down waves were slower.
 //
 // Balanced persistent grid: all tasks cost the same, so with n tasks and S
 // wave slots the kernel runs k = ceil(n/S) rounds on W = ceil(n/k) waves
@@ -27,11 +31,17 @@
 // pairs equal k.  Steps start at a task-dependent rotation of K so that
 // concurrent waves do not all read the same column offset of their rows.
 //
+// A chunk's tile t holds rows 16 t .. 16 t + 15 of the chunk; only its active
+// tiles (rows present) are loaded and multiplied, the count being uniform per
+// task.
+//
 // Column map: gated slices hold 64 output columns; weight row of tile j
 // (j = 0..3 gate, 4..7 up) for lane l is c0 + 4*(l%16) + (j%4), so a lane
 // owns four adjacent output columns (mode 2, the backward's recompute, stores
 // gate and up as well as SiLU(gate) * up).  Plain slices hold 128 columns: row
 // c0 + 8*(l%16) + j, eight adjacent output columns per lane.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -43,29 +53,37 @@ constexpr int SK = 128;  // K per step
 constexpr int QC = SK / 32;  // 16-byte chunks per lane, row and step
 
 constexpr int NT = 8;   // 16-row weight tiles per wave
+constexpr int MAXT = kStreamChunk / 16;  // 16-row token tiles per task at most
+static_assert(MAXT == 4, "the task dispatch covers 1 to 4 tiles");
 
 MOE_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Every lane loads unconditionally (rows past the expert's count read a valid
 // row of the chunk and their outputs are never stored), so the compiler can
 // count outstanding loads exactly.
-MOE_DEV void load_step(u32x4 (&b)[NT][QC], u32x4 (&a)[QC], const bf16_t* const (&brow)[NT],
-                       const bf16_t* arow, int koff) {
+template <int NTILE>
+MOE_DEV void load_step(u32x4 (&b)[NT][QC], u32x4 (&a)[NTILE][QC], const bf16_t* const (&brow)[NT],
+                       const bf16_t* const (&arow)[NTILE], int koff) {
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int q = 0; q < QC; ++q) b[j][q] = *reinterpret_cast<const u32x4*>(brow[j] + koff + q * 8);
 #pragma unroll
-  for (int q = 0; q < QC; ++q) a[q] = *reinterpret_cast<const u32x4*>(arow + koff + q * 8);
+  for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+    for (int q = 0; q < QC; ++q) a[t][q] = *reinterpret_cast<const u32x4*>(arow[t] + koff + q * 8);
 }
 
-MOE_DEV void mma_step(f32x4 (&acc)[NT], const u32x4 (&b)[NT][QC], const u32x4 (&a)[QC]) {
+template <int NTILE>
+MOE_DEV void mma_step(f32x4 (&acc)[NTILE][NT], const u32x4 (&b)[NT][QC], const u32x4 (&a)[NTILE][QC]) {
 #pragma unroll
   for (int q = 0; q < QC; ++q)
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[q]), as_bf16x8(b[j][q]), acc[j],
-                                                       0, 0, 0);
+    for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[t][q]), as_bf16x8(b[j][q]),
+                                                            acc[t][j], 0, 0, 0);
 }
 
 }  // namespace
@@ -117,32 +135,31 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
     const bool shared = lo >= g.E;
     const int cnt = shared ? g.T : cnt_s[lo];
     t.row_base = shared ? g.TK + (lo - g.E) * g.T : off_s[lo];
-    const int nch = (cnt + 15) >> 4;
+    const int nch = (cnt + kStreamChunk - 1) / kStreamChunk;
     const int local = task - cs_s[lo] * n_slices;
     t.slice = local / nch;
-    t.m0 = (local - t.slice * nch) * 16;
-    t.rows = min(16, cnt - t.m0);
+    t.m0 = (local - t.slice * nch) * kStreamChunk;
+    t.rows = min(kStreamChunk, cnt - t.m0);
     return t;
   };
-  // activation row of this lane (every lane a valid row of the chunk)
-  auto a_row = [&](const StreamTask& t) {
-    const int m = t.m0 + min(lane & 15, t.rows - 1);
-    if (GATED) return (t.e >= g.E) ? m : g.perm[t.row_base + m];
-    return t.row_base + m;
+  // activation row of this lane in each tile of the chunk (every lane a valid
+  // row of the chunk; tiles past the rows are not multiplied)
+  auto a_rows = [&](const StreamTask& t, int (&r)[MAXT]) {
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) {
+      const int m = t.m0 + min(16 * i + (lane & 15), t.rows - 1);
+      r[i] = GATED ? ((t.e >= g.E) ? m : g.perm[t.row_base + m]) : t.row_base + m;
+    }
   };
 
-  StreamTask cur = decode(wid);
-  int cur_row = a_row(cur);
-  for (int task = wid; task < n_tasks; task += active) {
-    // the next task's description and token row are fetched now and arrive
-    // while this task streams
-    const int ntask = task + active < n_tasks ? task + active : task;
-    const StreamTask nxt = decode(ntask);
-    const int nxt_row = a_row(nxt);
-
+  // one task with NTILE active 16-row tiles
+  auto run = [&](const StreamTask& cur, const int (&rws)[MAXT], int task, auto ntile_c) {
+    constexpr int NTILE = decltype(ntile_c)::value;
     const int e = cur.e, row_base = cur.row_base, m0 = cur.m0, rows = cur.rows;
     const int slice = cur.slice;
-    const bf16_t* arow = g.a + (size_t)cur_row * g.K + koff0;
+    const bf16_t* arow[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) arow[t] = g.a + (size_t)rws[t] * g.K + koff0;
     const bf16_t* brow[NT];
     const bf16_t* w0 = g.w0 + (size_t)e * g.N * g.K;
     if (GATED) {
@@ -159,56 +176,80 @@ __global__ __launch_bounds__(256, 1) void stream_gemm_kernel(StreamArgs g) {
       for (int j = 0; j < NT; ++j) brow[j] = w0 + (size_t)(c + j) * g.K + koff0;
     }
 
-    f32x4 acc[NT];
+    f32x4 acc[NTILE][NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int rot = (task * 7) % nsteps;
-    u32x4 b[NT][QC], a[QC];
+    u32x4 b[NT][QC], a[NTILE][QC];
     for (int s = 0; s < nsteps; ++s) {
       const int k = rot + s;
-      load_step(b, a, brow, arow, (k >= nsteps ? k - nsteps : k) * SK);
+      load_step<NTILE>(b, a, brow, arow, (k >= nsteps ? k - nsteps : k) * SK);
       __builtin_amdgcn_sched_barrier(0);
-      mma_step(acc, b, a);
+      mma_step<NTILE>(acc, b, a);
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // epilogue: lane holds rows 4*(lane/16)+t of the 16-row tile
+    // epilogue: in tile t, lane holds rows 16 t + 4*(lane/16) + v
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int m = m0 + 4 * (lane >> 4) + t;
-      if (m >= m0 + rows) continue;
-      bf16_t* dst = g.out + (size_t)(row_base + m) * g.N;
-      if (GATED) {
-        const int c = slice * 64 + 4 * (lane & 15);
-        uint2 pk;
-        pk.x = uint32_t(f32_to_bf16(siluf(acc[0][t]) * acc[4][t])) |
-               (uint32_t(f32_to_bf16(siluf(acc[1][t]) * acc[5][t])) << 16);
-        pk.y = uint32_t(f32_to_bf16(siluf(acc[2][t]) * acc[6][t])) |
-               (uint32_t(f32_to_bf16(siluf(acc[3][t]) * acc[7][t])) << 16);
-        *reinterpret_cast<uint2*>(dst + c) = pk;
-        if (MODE == 2) {  // the backward keeps G and U as well
-          const size_t o = (size_t)(row_base + m) * g.N + c;
-          uint2 pg, pu;
-          pg.x = uint32_t(f32_to_bf16(acc[0][t])) | (uint32_t(f32_to_bf16(acc[1][t])) << 16);
-          pg.y = uint32_t(f32_to_bf16(acc[2][t])) | (uint32_t(f32_to_bf16(acc[3][t])) << 16);
-          pu.x = uint32_t(f32_to_bf16(acc[4][t])) | (uint32_t(f32_to_bf16(acc[5][t])) << 16);
-          pu.y = uint32_t(f32_to_bf16(acc[6][t])) | (uint32_t(f32_to_bf16(acc[7][t])) << 16);
-          *reinterpret_cast<uint2*>(g.out_g + o) = pg;
-          *reinterpret_cast<uint2*>(g.out_u + o) = pu;
+    for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 16 * t + 4 * (lane >> 4) + v;
+        if (m >= m0 + rows) continue;
+        bf16_t* dst = g.out + (size_t)(row_base + m) * g.N;
+        const f32x4* ac = acc[t];
+        if (GATED) {
+          const int c = slice * 64 + 4 * (lane & 15);
+          uint2 pk;
+          pk.x = uint32_t(f32_to_bf16(siluf(ac[0][v]) * ac[4][v])) |
+                 (uint32_t(f32_to_bf16(siluf(ac[1][v]) * ac[5][v])) << 16);
+          pk.y = uint32_t(f32_to_bf16(siluf(ac[2][v]) * ac[6][v])) |
+                 (uint32_t(f32_to_bf16(siluf(ac[3][v]) * ac[7][v])) << 16);
+          *reinterpret_cast<uint2*>(dst + c) = pk;
+          if (MODE == 2) {  // the backward keeps G and U as well
+            const size_t o = (size_t)(row_base + m) * g.N + c;
+            uint2 pg, pu;
+            pg.x = uint32_t(f32_to_bf16(ac[0][v])) | (uint32_t(f32_to_bf16(ac[1][v])) << 16);
+            pg.y = uint32_t(f32_to_bf16(ac[2][v])) | (uint32_t(f32_to_bf16(ac[3][v])) << 16);
+            pu.x = uint32_t(f32_to_bf16(ac[4][v])) | (uint32_t(f32_to_bf16(ac[5][v])) << 16);
+            pu.y = uint32_t(f32_to_bf16(ac[6][v])) | (uint32_t(f32_to_bf16(ac[7][v])) << 16);
+            *reinterpret_cast<uint2*>(g.out_g + o) = pg;
+            *reinterpret_cast<uint2*>(g.out_u + o) = pu;
+          }
+        } else {
+          const int c = slice * 128 + 8 * (lane & 15);
+          u32x4 pk;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pk[q] = uint32_t(f32_to_bf16(ac[2 * q][v])) |
+                    (uint32_t(f32_to_bf16(ac[2 * q + 1][v])) << 16);
+          *reinterpret_cast<u32x4*>(dst + c) = pk;
         }
-      } else {
-        const int c = slice * 128 + 8 * (lane & 15);
-        u32x4 pk;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          pk[q] = uint32_t(f32_to_bf16(acc[2 * q][t])) |
-                  (uint32_t(f32_to_bf16(acc[2 * q + 1][t])) << 16);
-        *reinterpret_cast<u32x4*>(dst + c) = pk;
       }
+  };
+
+  StreamTask cur = decode(wid);
+  int cur_rows[MAXT];
+  a_rows(cur, cur_rows);
+  for (int task = wid; task < n_tasks; task += active) {
+    // the next task's description and token rows are fetched now and arrive
+    // while this task streams
+    const int ntask = task + active < n_tasks ? task + active : task;
+    const StreamTask nxt = decode(ntask);
+    int nxt_rows[MAXT];
+    a_rows(nxt, nxt_rows);
+    switch ((cur.rows + 15) >> 4) {  // uniform
+      case 4: run(cur, cur_rows, task, std::integral_constant<int, 4>{}); break;
+      case 3: run(cur, cur_rows, task, std::integral_constant<int, 3>{}); break;
+      case 2: run(cur, cur_rows, task, std::integral_constant<int, 2>{}); break;
+      default: run(cur, cur_rows, task, std::integral_constant<int, 1>{}); break;
     }
     cur = nxt;
-    cur_row = nxt_row;
+#pragma unroll
+    for (int i = 0; i < MAXT; ++i) cur_rows[i] = nxt_rows[i];
   }
 }
 
