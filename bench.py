@@ -46,8 +46,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
-    "decode": {"src_sha256": "5851aa178b2143b2af5a9c5b5a65bc21ed150f13e7758613b0d98bbef39241e6",
-             "fetch_kib": 8152229.7, "write_kib": 9216.0},
+    "decode": {"src_sha256": "f220324f51f858ced223435206b38325478b79340a9be9f7a6b9e84eb5ed2abb",
+             "fetch_kib": 7749117.0, "write_kib": 9216.1},
     "fp8": {"src_sha256": "414ae1717fa3b22e9cd9ca42fbbe792bfa816b3a9f1a619d6a72b43b595484d8",
             "fetch_kib": 4961546.6, "write_kib": 92203.6},
     "prefill": {"src_sha256": "d126ba0b0c9a91f2987070f4d6c384ffd6c20b9aed7e86ac42a42bfcdd1e0e3b",
