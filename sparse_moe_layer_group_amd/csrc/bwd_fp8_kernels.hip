@@ -61,12 +61,8 @@ constexpr int F8_CPW = F8_OP / 1024 / 4;        // 1 KB copies per operand and w
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
 
-MOE_DEV void copy16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
-}
-MOE_DEV void copy4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, voff, 0, 0, 0);
-}
+MOE_DEV void copy16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* dst) { copy_to_lds_async16(rs, voff, dst); }
+MOE_DEV void copy4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t* dst) { copy_to_lds_async4(rs, voff, dst); }
 
 template <int GROUP, int NSRC, typename TO, bool BN>
 __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {

@@ -170,10 +170,10 @@ __global__ __launch_bounds__(BG_NT, 2) void dgrad_gemm_kernel(BwdArgs g) {
     const __amdgpu_buffer_rsrc_t br = second ? br1 : br0;
 #pragma unroll
     for (int i = 0; i < DG_ACP; ++i)
-      copy16_to_lds(ar, aoff[i] + uint32_t(kk * BG_K * 2), st + 16 * (DG_ACP * wave + i) * BG_K);
+      copy_to_lds_async16(ar, aoff[i] + uint32_t(kk * BG_K * 2), st + 16 * (DG_ACP * wave + i) * BG_K);
 #pragma unroll
     for (int i = 0; i < DG_BCP; ++i)
-      copy16_to_lds(br, boff[i] + uint32_t(kk * BG_K) * uint32_t(N) * 2u,
+      copy_to_lds_async16(br, boff[i] + uint32_t(kk * BG_K) * uint32_t(N) * 2u,
                     st + BG_M * BG_K + 2 * (DG_BCP * wave + i) * DG_N);
   };
 
@@ -355,12 +355,12 @@ __global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
       bf16_t* d = Bs + (kt & 1) * DT_BSTAGE + 2 * DT_BCP * cw * DT_N;
       const uint32_t ko = kk * uint32_t(DT_K) * uint32_t(N) * 2u;
 #pragma unroll
-      for (int i = 0; i < DT_BCP; ++i) copy16_to_lds(rs, off[i] + ko, d + 2 * i * DT_N);
+      for (int i = 0; i < DT_BCP; ++i) copy_to_lds_async16(rs, off[i] + ko, d + 2 * i * DT_N);
     } else {
       bf16_t* d = As + (kt & 1) * DT_ASTAGE + 8 * DT_ACP * cw * DT_K;
       const uint32_t ko = kk * uint32_t(DT_K) * 2u;
 #pragma unroll
-      for (int i = 0; i < DT_ACP; ++i) copy16_to_lds(rs, off[i] + ko, d + 8 * i * DT_K);
+      for (int i = 0; i < DT_ACP; ++i) copy_to_lds_async16(rs, off[i] + ko, d + 8 * i * DT_K);
     }
   };
 
@@ -591,13 +591,13 @@ __global__ __launch_bounds__(BG_NT, 2) void wgrad_gemm_kernel(BwdArgs g) {
     for (int i = 0; i < WG_ACP; ++i) {
       const int r = k * BG_K + akr[i];
       const uint32_t o = r < cnt ? (uint32_t(row_base + r) * uint32_t(M) + acol[i]) * 2u : 0xfffffff0u;
-      copy16_to_lds(ar, o, st + 4 * (WG_ACP * wave + i) * BG_M);
+      copy_to_lds_async16(ar, o, st + 4 * (WG_ACP * wave + i) * BG_M);
     }
 #pragma unroll
     for (int i = 0; i < WG_BCP; ++i) {
       const int r = k * BG_K + bkr[i];
       const uint32_t o = r < cnt ? (uint32_t(row_base + r) * uint32_t(N) + bcol[i]) * 2u : 0xfffffff0u;
-      copy16_to_lds(br, o, st + BG_K * BG_M + 2 * (WG_BCP * wave + i) * WG_N);
+      copy_to_lds_async16(br, o, st + BG_K * BG_M + 2 * (WG_BCP * wave + i) * WG_N);
     }
   };
 
@@ -780,14 +780,14 @@ __global__ __launch_bounds__(WS_NT, WS_BPC * (4 + WS_CW) / 4) void wgrad_ws_kern
         const int r = r0 + akr[i];
         const uint32_t o =
             r < lt.cnt ? (uint32_t(lt.base + r) * uint32_t(M) + uint32_t(lt.m0 + ach[i])) * 2u : 0xfffffff0u;
-        copy16_to_lds(ar, o, st + 4 * (WS_ACP * c + i) * BG_M);
+        copy_to_lds_async16(ar, o, st + 4 * (WS_ACP * c + i) * BG_M);
       }
 #pragma unroll
       for (int i = 0; i < WS_BCP; ++i) {
         const int r = r0 + bkr[i];
         const uint32_t o =
             r < lt.cnt ? (uint32_t(lt.base + r) * uint32_t(N) + uint32_t(lt.n0 + bch[i])) * 2u : 0xfffffff0u;
-        copy16_to_lds(br, o, st + BG_K * BG_M + 2 * (WS_BCP * c + i) * WG_N);
+        copy_to_lds_async16(br, o, st + BG_K * BG_M + 2 * (WS_BCP * c + i) * WG_N);
       }
       ++issued;
       if (++lk * BG_K >= lt.cnt) {
