@@ -225,9 +225,9 @@ __global__ __launch_bounds__(512, 1) void router_tile_kernel(const bf16_t* __res
     bf16_t* a = As + stage * RT_ASTAGE + (16 * ACPW * wave) * RT_TBK;
     bf16_t* b = Bs + stage * RT_BSTAGE + (16 * BCPW * wave) * RT_TBK;
 #pragma unroll
-    for (int i = 0; i < ACPW; ++i) copy16_to_lds(ars, aoff[i] + ka, a + 16 * i * RT_TBK);
+    for (int i = 0; i < ACPW; ++i) copy_to_lds_async16(ars, aoff[i] + ka, a + 16 * i * RT_TBK);
 #pragma unroll
-    for (int i = 0; i < BCPW; ++i) copy16_to_lds(brs, boff[i] + kb, b + 16 * i * RT_TBK);
+    for (int i = 0; i < BCPW; ++i) copy_to_lds_async16(brs, boff[i] + kb, b + 16 * i * RT_TBK);
   };
 
   f32x16 acc[2][2];
