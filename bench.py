@@ -48,21 +48,21 @@ COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buff
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
     "decode": {"src_sha256": "f220324f51f858ced223435206b38325478b79340a9be9f7a6b9e84eb5ed2abb",
              "fetch_kib": 7749117.0, "write_kib": 9216.1},
-    "fp8": {"src_sha256": "414ae1717fa3b22e9cd9ca42fbbe792bfa816b3a9f1a619d6a72b43b595484d8",
-            "fetch_kib": 4961546.6, "write_kib": 92203.6},
-    "prefill": {"src_sha256": "d126ba0b0c9a91f2987070f4d6c384ffd6c20b9aed7e86ac42a42bfcdd1e0e3b",
-              "fetch_kib": 12190886.6, "write_kib": 294912.0},
-    "backward_prefill_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
-                            "fetch_kib": 6394862.8, "write_kib": 44214735.7},
-    "backward_decode_bf16": {"src_sha256": "664296ea8707f898cc602acc837672eaf948c7574f06037d93bf29cf2eba0979",
-                            "fetch_kib": 85678.5, "write_kib": 44238395.1},
+    "fp8": {"src_sha256": "4fd6e2e96886b83d35f9622100f1a7238812d9c3f0fddd18a8a2400198295c9d",
+            "fetch_kib": 4964611.9, "write_kib": 92203.6},
+    "prefill": {"src_sha256": "ee4cbfbbd3dcd9296fc1252514015ba2e84d5ede317bbd733ff4bd876784c30a",
+              "fetch_kib": 12196422.0, "write_kib": 294912.0},
+    "backward_prefill_bf16": {"src_sha256": "e1b37b1c6ff208e6636a40082ff83313615a61301e54f45334c9305577a7016b",
+                            "fetch_kib": 6421738.9, "write_kib": 44214469.8},
+    "backward_decode_bf16": {"src_sha256": "e1b37b1c6ff208e6636a40082ff83313615a61301e54f45334c9305577a7016b",
+                            "fetch_kib": 85693.1, "write_kib": 44233619.9},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "d126ba0b0c9a91f2987070f4d6c384ffd6c20b9aed7e86ac42a42bfcdd1e0e3b",
-                "busy": 0.578, "clock_ghz": 1.53, "executed_bf16_tflop": 4.56},
+    "prefill": {"src_sha256": "ee4cbfbbd3dcd9296fc1252514015ba2e84d5ede317bbd733ff4bd876784c30a",
+                "busy": 0.576, "clock_ghz": 1.54, "executed_bf16_tflop": 4.56},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
@@ -71,9 +71,9 @@ KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
                   "skew": _COMMON_SOURCES + ("stream_gemm.hip", "tile_gemm.hip"),
                   "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",),
                   # backward: the weight-gradient stage (all its launches in one call)
-                  "backward_prefill_bf16": _COMMON_SOURCES + ("bwd.h", "bwd_kernels.hip"),
-                  "backward_decode_bf16": _COMMON_SOURCES + ("bwd.h", "bwd_kernels.hip"),
-                  "backward_prefill_e4m3": _COMMON_SOURCES + ("bwd.h", "bwd_fp8_kernels.hip")}
+                  "backward_prefill_bf16": _COMMON_SOURCES + ("lds_async.h", "bwd.h", "bwd_kernels.hip"),
+                  "backward_decode_bf16": _COMMON_SOURCES + ("lds_async.h", "bwd.h", "bwd_kernels.hip"),
+                  "backward_prefill_e4m3": _COMMON_SOURCES + ("lds_async.h", "bwd.h", "bwd_fp8_kernels.hip")}
 
 
 def log(msg):

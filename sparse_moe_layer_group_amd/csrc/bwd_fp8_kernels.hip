@@ -30,6 +30,7 @@
 // scales.
 #include "bwd.h"
 #include "common.h"
+#include "lds_async.h"
 
 namespace moe {
 

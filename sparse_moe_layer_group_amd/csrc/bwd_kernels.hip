@@ -34,6 +34,7 @@
 
 #include "bwd.h"
 #include "common.h"
+#include "lds_async.h"
 
 namespace moe {
 

@@ -135,24 +135,4 @@ MOE_DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff, bf16_t* dst
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
 }
 
-// The same copies issued from inline assembly (4 or 16 bytes per lane), for
-// kernels that read LDS with the transposing ds_read_b64_tr_b{8,16}: this
-// compiler cannot tell those reads apart from the copies' targets and makes
-// each of them wait until every copy in flight has landed (vmcnt(0)), which
-// turns a ring of stages into synchronous copies.  Issued as assembly, the
-// copies are outside that analysis.  A kernel using these orders its copies
-// and LDS reads with its own vmcnt waits and barriers, and must not have a
-// vector-memory load of its own in flight across them (the compiler would
-// count its waits for that load without these copies).  M0 takes the LDS
-// address through the operand constraint; the s_nop covers the M0 -> LDS DMA
-// hazard.
-MOE_DEV void copy_to_lds_async16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* dst) {
-  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)dst));
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
-}
-MOE_DEV void copy_to_lds_async4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* dst) {
-  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)dst));
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
-}
-
 }  // namespace moe

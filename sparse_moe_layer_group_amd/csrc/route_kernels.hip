@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "lds_async.h"
 #include "kernels.h"
 
 namespace moe {
