@@ -58,11 +58,14 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
                             "fetch_kib": 85693.1, "write_kib": 44233619.9},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
-# SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
+# SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F8, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
     "prefill": {"src_sha256": "ee4cbfbbd3dcd9296fc1252514015ba2e84d5ede317bbd733ff4bd876784c30a",
                 "busy": 0.576, "clock_ghz": 1.54, "executed_bf16_tflop": 4.56},
+    # (SQ_INSTS_VALU_MFMA_MOPS_F8; profiles/moe_forward_fp8_e4m3.md)
+    "fp8": {"src_sha256": "4fd6e2e96886b83d35f9622100f1a7238812d9c3f0fddd18a8a2400198295c9d",
+            "busy": 0.234, "clock_ghz": 1.96, "executed_f8_tflop": 2.40},
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
@@ -164,11 +167,13 @@ def summarize_profile(path):
                 per[kk][r["Counter_Name"]].append(float(r["Counter_Value"]))
                 if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                     dur[kk].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
-            need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
-            table = [(kk, c) for kk, c in per.items() if all(n in c for n in need) and dur[kk]]
-            if table:
+            for fmt in ("BF16", "F8"):  # executed flops = MOPS x 512
+                need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_" + fmt)
+                table = [(kk, c) for kk, c in per.items() if all(n in c for n in need) and dur[kk]]
+                if not table:
+                    continue
                 print(f"{'kernel':40s} {'id':>6s} {'us':>9s} {'clock GHz':>10s} {'MFMA busy':>10s} "
-                      f"{'bf16 TFLOP':>11s} {'TFLOP/s':>9s}")
+                      f"{fmt.lower() + ' TFLOP':>11s} {'TFLOP/s':>9s}")
                 for (k, kid), c in table:
                     t = sum(dur[(k, kid)]) / len(dur[(k, kid)])
                     grbm = sum(c[need[0]]) / len(c[need[0]])
@@ -402,6 +407,7 @@ def bench_forward(name, args, np, torch, moe, S, dev, primary):
         roofline["mfma_counters"] = measured_mfma(c.name)
     if c.w_dtype == "e4m3":   # the same kernel against the fp8 matrix cores
         roofline["mfma_frac_e4m3"] = round(gu_flops / gu_s / 1e12 / MFMA_PEAK_TFLOPS["e4m3"], 4)
+        roofline["mfma_counters"] = measured_mfma(c.name)
     layer = {"ms": round(ms_step, 4), "alg_bytes": int(layer_bytes), "alg_flops": int(layer_flops),
              "hbm_frac": round(layer_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
              "mfma_frac": round(layer_flops / (ms_step / 1e3) / 1e12 /
