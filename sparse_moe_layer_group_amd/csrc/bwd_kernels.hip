@@ -449,54 +449,82 @@ __global__ __launch_bounds__(DT_NT, 1) void dgrad_tile_kernel(BwdArgs g) {
     default: mainloop(std::integral_constant<int, 0>{}); break;
   }
 
-  // epilogue.  32x32 accumulator v of lane l: row 8 (v/4) + 4 (l/32) + v%4, column l%32
-  float part[DT_MBW][16];  // MODE 0 with g.dgp: this lane's sum of dH * H per row
-#pragma unroll
-  for (int i = 0; i < DT_MBW; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) part[i][v] = 0.f;
+  // epilogue.  32x32 accumulator v of lane l: row 8 (v/4) + 4 (l/32) + v%4,
+  // column l%32.  Each wave stages one 32-row block of its 64 columns at a
+  // time (float32) in a slot of its own; a lane then takes 8 consecutive
+  // columns of a row, so G and U are read and dG, dU (dX) written 16 bytes a
+  // lane instead of 2 bytes per accumulator element.
+  constexpr int EP_PITCH = 64 * 4 + 16;  // staged row bytes (rows r, r + 4 in other banks)
+  static_assert(DT_NWAVE * 32 * EP_PITCH + DT_WN * DT_M * 4 <= 2 * (DT_ASTAGE + DT_BSTAGE) * 2,
+                "the staging slots and row sums fit the stages");
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef __attribute__((address_space(3))) float lds_f32;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  __syncthreads();  // every wave is done with the stages
+  lds_u8* slot = (lds_u8*)dsm + wave * 32 * EP_PITCH;
+  lds_f32* red = (lds_f32*)((lds_u8*)dsm + DT_NWAVE * 32 * EP_PITCH);  // [DT_WN][DT_M] row sums
+  const int er = lane >> 3, ec = 8 * (lane & 7);  // row within an 8-row pass, first column
 #pragma unroll
   for (int i = 0; i < DT_MBW; ++i) {
     if (i >= mact) continue;  // uniform
 #pragma unroll
-    for (int j = 0; j < DT_NJ; ++j) {
-      const int col = n0 + wn * 64 + 32 * j + (lane & 31);
+    for (int j = 0; j < DT_NJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 32 * DT_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r >= rows) continue;
-        const size_t o = size_t(row_base + m0 + r) * N + col;
-        const float d = acc[i][j][v];
+      for (int v = 0; v < 16; ++v)
+        *(lds_f32*)(slot + (8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP_PITCH + 4 * (32 * j + (lane & 31))) =
+            acc[i][j][v];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = 8 * q + er;                     // row within the block
+      const int r = wm * 32 * DT_MBW + 32 * i + rr;  // row within the tile
+      const f32x4 d0 = *(const lds_f32x4*)(slot + rr * EP_PITCH + 4 * ec);
+      const f32x4 d1 = *(const lds_f32x4*)(slot + rr * EP_PITCH + 4 * ec + 16);
+      const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      float psum = 0.f;  // MODE 0: sum of dH * H over these 8 columns, in column order
+      if (r < rows) {
+        const size_t o = size_t(row_base + m0 + r) * N + n0 + wn * 64 + ec;
+        u32x4 w0;
         if (MODE == 0) {
-          const float G = bf16_to_f32(g.gst[o]), U = bf16_to_f32(g.ust[o]);
-          const float sg = sigm(G);
-          g.dgst[o] = f32_to_bf16(d * U * sg * (1.0f + G * (1.0f - sg)));
-          const float du = d * G * sg;  // dH SiLU(G)
-          g.dust[o] = f32_to_bf16(du);
-          part[i][v] = fmaf(du, U, part[i][v]);  // dH H, H = SiLU(G) U
+          const u32x4 gr = *reinterpret_cast<const u32x4*>(g.gst + o);
+          const u32x4 ur = *reinterpret_cast<const u32x4*>(g.ust + o);
+          u32x4 w1;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t pg = 0, pu = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float G = bf16_to_f32(bf16_t(gr[k] >> (16 * h))), U = bf16_to_f32(bf16_t(ur[k] >> (16 * h)));
+              const float dh = d[2 * k + h];
+              const float sg = sigm(G);
+              const float du = dh * G * sg;  // dH SiLU(G)
+              pg |= uint32_t(f32_to_bf16(dh * U * sg * (1.0f + G * (1.0f - sg)))) << (16 * h);
+              pu |= uint32_t(f32_to_bf16(du)) << (16 * h);
+              psum = fmaf(du, U, psum);      // dH H, H = SiLU(G) U
+            }
+            w0[k] = pg;
+            w1[k] = pu;
+          }
+          *reinterpret_cast<u32x4*>(g.dgst + o) = w0;
+          *reinterpret_cast<u32x4*>(g.dust + o) = w1;
         } else {
-          g.dxst[o] = f32_to_bf16(d);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            w0[k] = uint32_t(f32_to_bf16(d[2 * k])) | (uint32_t(f32_to_bf16(d[2 * k + 1])) << 16);
+          *reinterpret_cast<u32x4*>(g.dxst + o) = w0;
         }
       }
-    }
-  }
-  if (MODE == 0 && g.dgp != nullptr) {
-    // row sums over the tile's 256 columns: 32 lanes of a half-wave (fixed
-    // butterfly), then the 4 waves along N through LDS in wave order
-    float* red = reinterpret_cast<float*>(dsm);  // [DT_WN][DT_M]
-    __syncthreads();  // every wave is done with the stages
+      if (MODE == 0 && g.dgp != nullptr) {
+        // the row's sum over this wave's 64 columns: its 8 lanes, fixed butterfly
 #pragma unroll
-    for (int i = 0; i < DT_MBW; ++i) {
-      if (i >= mact) continue;  // uniform
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float t = part[i][v];
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) t += __shfl_xor(t, off, 32);
-        if ((lane & 31) == 0)
-          red[wn * DT_M + wm * 32 * DT_MBW + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)] = t;
+        for (int off = 1; off < 8; off <<= 1) psum += __shfl_xor(psum, off, 8);
+        if ((lane & 7) == 0) red[wn * DT_M + r] = psum;
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  if (MODE == 0 && g.dgp != nullptr) {
+    // row sums over the tile's 256 columns: the 4 waves along N in wave order
     __syncthreads();
     if (tid < rows) {
       const int wmr = tid / (32 * DT_MBW), mb = (tid - wmr * 32 * DT_MBW) >> 5;
