@@ -242,15 +242,27 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)(st + FS_ASTAGE + srow0 * 4), 4,
                                              soff + kc * 4u, 0, 0, 0);
   };
-  // weight-row copies of block kb into private stage kb % FS_NSB
+  // weight-row copies of block kb into private stage kb % FS_NSB.  An expert
+  // with one row tile reads its weights once: those copies are non-temporal
+  // (streamed past the caches; 2350 -> 2280 us for gate/up at 4096 tokens).
+  // An expert with more row tiles keeps them cacheable for its other tiles.
+  const bool once = n_mt == 1;
   auto copy_b = [&](int kb) {
     const uint32_t ko = uint32_t(kblock(kb)) * 128u;
     uint8_t* st = bring + (kb % FS_NSB) * FS_BWAVE;
+    if (once) {
 #pragma unroll
-    for (int i = 0; i < FS_BCOPY; ++i) {
-      const __amdgpu_buffer_rsrc_t rs = (GATED && i >= FS_BCOPY / 2) ? wr1 : wr0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + 1024 * i), 16, boff[i] + ko, 0,
-                                               0, 0);
+      for (int i = 0; i < FS_BCOPY; ++i) {
+        const __amdgpu_buffer_rsrc_t rs = (GATED && i >= FS_BCOPY / 2) ? wr1 : wr0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + 1024 * i), 16, boff[i] + ko, 0, 0,
+                                                 2 /* nt */);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FS_BCOPY; ++i) {
+        const __amdgpu_buffer_rsrc_t rs = (GATED && i >= FS_BCOPY / 2) ? wr1 : wr0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + 1024 * i), 16, boff[i] + ko, 0, 0, 0);
+      }
     }
   };
 
