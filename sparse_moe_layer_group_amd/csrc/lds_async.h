@@ -16,10 +16,17 @@ namespace moe {
 // vector-memory load of its own in flight across them (the compiler would
 // count its waits for that load without these copies).  M0 takes the LDS
 // address through the operand constraint; the s_nop covers the M0 -> LDS DMA
-// hazard.
+// hazard.  The resource and the LDS address must be wave-uniform: the
+// compiler places a divergent value for an "s" operand in vector registers,
+// which this instruction cannot take.
 MOE_DEV void copy_to_lds_async16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* dst) {
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)dst));
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+// the 16-byte copy with the non-temporal hint, for data read once
+MOE_DEV void copy_to_lds_async16_nt(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* dst) {
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)dst));
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rs), "{m0}"(lds) : "memory");
 }
 MOE_DEV void copy_to_lds_async4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* dst) {
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)dst));
