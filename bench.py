@@ -46,8 +46,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
-    "decode": {"src_sha256": "f220324f51f858ced223435206b38325478b79340a9be9f7a6b9e84eb5ed2abb",
-             "fetch_kib": 7749117.0, "write_kib": 9216.1},
+    "decode": {"src_sha256": "c958487bd206fb3715457dc850ca5415a567a010a08736def4e085277c001ae9",
+             "fetch_kib": 7495490.2, "write_kib": 9216.0},
     "fp8": {"src_sha256": "4fd6e2e96886b83d35f9622100f1a7238812d9c3f0fddd18a8a2400198295c9d",
             "fetch_kib": 4964611.9, "write_kib": 92203.6},
     "prefill": {"src_sha256": "ee4cbfbbd3dcd9296fc1252514015ba2e84d5ede317bbd733ff4bd876784c30a",
@@ -69,9 +69,9 @@ MEASURED_MFMA = {
 }
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
-KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("stream_gemm.hip",),
+KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("lds_async.h", "stream_gemm.hip"),
                   "prefill": _COMMON_SOURCES + ("tile_gemm.hip",),
-                  "skew": _COMMON_SOURCES + ("stream_gemm.hip", "tile_gemm.hip"),
+                  "skew": _COMMON_SOURCES + ("lds_async.h", "stream_gemm.hip", "tile_gemm.hip"),
                   "fp8": _COMMON_SOURCES + ("fp8_kernels.hip",),
                   # backward: the weight-gradient stage (all its launches in one call)
                   "backward_prefill_bf16": _COMMON_SOURCES + ("lds_async.h", "bwd.h", "bwd_kernels.hip"),
