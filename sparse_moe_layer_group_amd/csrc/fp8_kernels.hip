@@ -73,10 +73,20 @@ hipError_t launch_quant_1x128(const bf16_t* x, long long rows, int C, uint8_t* q
 // Tile: kTileM8 (192) token rows x 256 weight rows.  Eight waves, two per
 // SIMD; wave w owns 32 weight rows (gate/up: 16 columns of W_gate and the
 // same 16 of W_up; down: 32 columns of W_down) against all 192 token rows, as
-// 12 x 2 blocks of v_mfma_scale_f32_16x16x128_f8f6f4.  One such MFMA covers a
+// 2 x 12 blocks of v_mfma_scale_f32_16x16x128_f8f6f4.  One such MFMA covers a
 // whole 128-wide K block, so its result is the block's full-precision
 // partial product: it is scaled by (row scale * weight-block scale) and added
 // to the float32 accumulator at once (hardware block scales left at 1).
+//
+// The weight fragment is the MFMA's first operand, so a lane's four results
+// of a block are four adjacent output columns of one token row: they share
+// one row scale and one weight-block scale, and the promotion takes one
+// multiply per lane and block pair (two for gate/up) besides the four
+// multiply-adds per block.  (With the token rows as the first operand each
+// result had a row of its own: one multiply per result, 8 rather than 5
+// vector instructions per MFMA for gate/up, and four times the LDS bytes for
+// the row scales.)  The MFMAs of row block i + 1 are issued before the
+// promotion of block i, so the vector ALU works while the matrix core does.
 //
 // Operand bytes: lane l holds, for its row (token or weight) l % 16, the two
 // 16-byte chunks g and g + 4 of the 128-byte block, g = l / 16.  Both
@@ -86,41 +96,39 @@ hipError_t launch_quant_1x128(const bf16_t* x, long long rows, int C, uint8_t* q
 // instruction; chunk c of row r stored at position c ^ (r % 8)):
 //   - weight rows: each wave copies its own 32 rows into a private LDS ring
 //     of FS_NSB blocks; a block's stage is refilled as soon as the wave has
-//     read its fragments into registers, so FS_NSB blocks (96 KB per CU)
-//     are in flight while one is multiplied.  HBM's loaded latency of a few
-//     microseconds needs about that much to stream at full bandwidth;
+//     read its fragments into registers, so FS_NSB blocks (64 KB per CU)
+//     are in flight while one is multiplied;
 //   - token rows and their scales: shared by all waves, a ring of FS_NSA
-//     blocks, FS_NSA - 1 ahead (they mostly hit L2).
+//     blocks, FS_NSA - 1 ahead.
 // The waits are explicit vmcnt counts.  Per block kb: wait until this wave's
-// copies of kb have landed (a wave's copies complete in issue order; the
-// token rows of kb are issued one block before use, after the weight rows of
-// kb), workgroup barrier (everyone's token rows of kb are in LDS and everyone
-// is done with kb-1), read the weight fragments of kb, issue the token copies
-// of kb+1 into the stage of kb-1 and the weight copies of kb+FS_NSB into the
-// stage just read, multiply block kb.  Blocks past the end re-read the last
-// block so that every iteration issues the same copies.
+// copies of kb have landed (a wave's copies complete in issue order),
+// workgroup barrier (everyone's token rows of kb are in LDS and everyone is
+// done with kb-1), read the weight fragments of kb, issue the token copies of
+// kb+2 into the stage of kb-1 and the weight copies of kb+2 into the stage
+// just read, multiply block kb.  Blocks past the end re-read the last block
+// so that every iteration issues the same copies.
 //
 // Gate/up tiles hold 128 columns of W_gate and the same 128 of W_up, exactly
 // one 1x128 slice of the SwiGLU output H: the epilogue forms SiLU(gate) * up,
 // reduces each row's max-abs across the eight waves through LDS, and writes H
-// as E4M3 codes plus one scale per row.
+// as E4M3 codes (four adjacent columns per 4-byte store) plus one scale per
+// row.
 //
-// What bounds it: the float32 promotion after every 128-wide K block costs
-// one multiply-add (and, gate/up, one multiply) per output element per block
-// on the vector ALUs, about as many lane-cycles as the MFMAs spend on the
-// block, and every wave reads all 192 token rows' fragments from LDS.  At
-// 4096 tokens the multiply side alone (no copies) measured 1.72 ms of the
-// gate/up GEMM's 2.4 ms, copies alone 1.86 ms; the weights stream at about
-// 3.2 TB/s.  Deeper copy rings (3 weight blocks in flight instead of 2) and
-// a per-workgroup rotation of the K order measured no faster.
+// Measured at 4096 tokens, gate/up on one box: 2300 us as first built (token
+// rows as the first operand, MFMAs and promotion of a block back to back),
+// 2160 us with the promotion of block i after the MFMAs of block i + 1, 1910
+// us with the weights as the first operand.  Token rows two blocks ahead
+// instead of one (with two weight blocks in flight instead of three) changed
+// gate/up by under 1% and down by -2%.  A per-workgroup rotation of the K
+// order measured no faster.
 namespace {
 
 constexpr int FS_TBM = kTileM8;                  // token rows per tile
 constexpr int FS_RB = FS_TBM / 16;               // 16-row MFMA blocks
 constexpr int FS_TBN = 256;                      // weight rows per tile
 constexpr int FS_NWAVE = 8, FS_NTHREAD = 64 * FS_NWAVE;
-constexpr int FS_NSA = 2;                        // shared LDS stages of token rows
-constexpr int FS_NSB = 3;                        // private LDS stages of weight rows per wave
+constexpr int FS_NSA = 3;                        // shared LDS stages of token rows
+constexpr int FS_NSB = 2;                        // private LDS stages of weight rows per wave
 constexpr int FS_ACOPY = FS_TBM / 8 / FS_NWAVE;  // 1 KB token-row copies per wave per block
 constexpr int FS_BCOPY = FS_TBN / 8 / FS_NWAVE;  // 1 KB weight-row copies per wave per block
 constexpr int FS_ASTAGE = FS_TBM * 128;          // code bytes per token stage
@@ -131,7 +139,7 @@ constexpr int FS_ACOPIES = FS_ACOPY + 1;         // token-row copies + scale cop
 static_assert(FS_TBM == 192, "scale copies: three waves of 64 rows");
 static_assert(FS_TBM % 32 == 0 && (FS_TBM / 8) % FS_NWAVE == 0 && FS_BCOPY == 4, "tile configuration");
 static_assert(FS_BBASE + FS_NWAVE * FS_NSB * FS_BWAVE <= 160 * 1024, "LDS per workgroup");
-static_assert(FS_NSA == 2 && FS_NSB == 3, "the prologue and wait count below assume this ring");
+static_assert(FS_NSA == 3 && FS_NSB == 2, "the prologue and wait count below assume this ring");
 
 }  // namespace
 
@@ -289,55 +297,74 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
         __builtin_amdgcn_readlane(__float_as_int(kr < 64 ? swv0[0] : swv0[1]), kr & 63));
     const float sb1 = __int_as_float(
         __builtin_amdgcn_readlane(__float_as_int(kr < 64 ? swv1[0] : swv1[1]), kr & 63));
-    // token fragments and row scales are read two row blocks ahead of their
-    // MFMAs; scheduling barriers keep the reads there
+    // token fragments and row scales are read three row blocks ahead of
+    // their promotion, two ahead of their MFMAs; the MFMAs of row block i + 1
+    // are issued before the promotion of block i, so the vector ALU works
+    // while the matrix core does
     i32x8 af[NRB];
-    f32x4 sa[NRB];
+    float sa[NRB];
     auto rd = [&](int i) {
       af[i] = frag(st, 16 * i + c16);
-      sa[i] = *reinterpret_cast<const f32x4*>(sc + 16 * i + 4 * g4);
+      sa[i] = sc[16 * i + c16];
     };
     rd(0);
     if (NRB > 1) rd(1);
+    if (NRB > 2) rd(2);
     const float sbb = GATED ? sb1 : sb0;
+    f32x4 t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, af[0], zero, 0, 0, 0, 127, 0, 127);
+    f32x4 t1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, af[0], zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
-      if (i + 2 < NRB) rd(i + 2);
+      if (i + 3 < NRB) rd(i + 3);
       __builtin_amdgcn_sched_barrier(0);
-      const f32x4 t0 =
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], b0, zero, 0, 0, 0, 127, 0, 127);
-      const f32x4 t1 =
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], b1, zero, 0, 0, 0, 127, 0, 127);
+      f32x4 u0 = zero, u1 = zero;
+      if (i + 1 < NRB) {
+        u0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b0, af[i + 1], zero, 0, 0, 0, 127, 0, 127);
+        u1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b1, af[i + 1], zero, 0, 0, 0, 127, 0, 127);
+      }
+      const float s0 = sa[i] * sb0, s1 = GATED ? sa[i] * sbb : s0;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        acc[i][0][v] = fmaf(t0[v], sa[i][v] * sb0, acc[i][0][v]);
-        acc[i][1][v] = fmaf(t1[v], sa[i][v] * sbb, acc[i][1][v]);
+        acc[i][0][v] = fmaf(t0[v], s0, acc[i][0][v]);
+        acc[i][1][v] = fmaf(t1[v], s1, acc[i][1][v]);
       }
+      if (i + 1 < NRB) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, GATED ? 5 : 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      t0 = u0;
+      t1 = u1;
     }
   };
 
   // Issue order (W = weight rows, A = token rows and scales):
-  //   prologue W0 W1 A0 W2; block kb: A(kb+1) W(kb+3)
-  // At the top of block kb the copies issued after A(kb) are exactly one
-  // weight block (W(kb+2)), and W(kb) was issued before A(kb): waiting until
-  // at most FS_BCOPY copies are in flight completes both.  The wave then
-  // reads its weight fragments of kb into registers, which frees its weight
-  // stage of kb for W(kb+3): three weight blocks stay in flight.
+  //   prologue W0 W1 A0 A1; block kb: A(kb+2) W(kb+2)
+  // At the top of block kb >= 1 the copies issued after W(kb) are exactly
+  // A(kb+1) and W(kb+1), and A(kb) was issued before W(kb): waiting until at
+  // most FS_ACOPIES + FS_BCOPY copies are in flight completes both (before
+  // block 0, at most FS_ACOPIES: only A1 follows A0).  The wave then reads
+  // its weight fragments of kb into registers, which frees its weight stage
+  // of kb for W(kb+2).
   // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt/lgkmcnt at maxima.
-  constexpr int VMW = FS_BCOPY;
+  constexpr int VMW = FS_BCOPY + FS_ACOPIES;
   constexpr int WAITIMM = (VMW & 15) | ((VMW >> 4) << 14) | 0x70 | 0xf00;
+  constexpr int VMW0 = FS_ACOPIES;
+  constexpr int WAITIMM0 = (VMW0 & 15) | ((VMW0 >> 4) << 14) | 0x70 | 0xf00;
   auto mainloop = [&](auto mact_c) {
     copy_b(0);
     copy_b(1);
     copy_a(0);
-    copy_b(2);
+    copy_a(1);
+    __builtin_amdgcn_s_waitcnt(WAITIMM0);  // W0, W1, A0 landed
     for (int kb = 0; kb < KB; ++kb) {
       __builtin_amdgcn_s_waitcnt(WAITIMM);  // this wave's token and weight rows of kb landed
       __builtin_amdgcn_s_barrier();         // everyone's; everyone is done with kb-1
       const uint8_t* bst = bring + (kb % FS_NSB) * FS_BWAVE;
       const i32x8 b0 = frag(bst, c16), b1 = frag(bst, 16 + c16);
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the weight stage of kb is free
-      copy_a(kb + 1);                       // into the token stage of kb-1
+      copy_a(kb + 2);                       // into the token stage of kb-1
       copy_b(kb + FS_NSB);                  // into this wave's weight stage of kb
       compute(kb, b0, b1, mact_c);
     }
@@ -352,7 +379,8 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
     default: mainloop(std::integral_constant<int, 1>{}); break;
   }
 
-  // ---- epilogue.  16x16 accumulator v of lane l: row 4*(l/16) + v, column l%16
+  // ---- epilogue.  16x16 accumulator v of lane l (weights as the MFMA's
+  // first operand): column 4*(l/16) + v of the block, token row l%16
   if (GATED) {
     // H = SiLU(gate) * up for the tile's 128 columns (one 1x128 slice per row)
     float* red = reinterpret_cast<float*>(smem8);  // [NWAVE][TBM] row max-abs per wave
@@ -361,32 +389,33 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
 #pragma unroll
     for (int i = 0; i < FS_RB; ++i) {
       if (2 * mact <= i) continue;  // uniform
+      float m = 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         h[i][v] = siluf(acc[i][0][v]) * acc[i][1][v];
-        float m = fabsf(h[i][v]);
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-        if (c16 == 0) red[wave * FS_TBM + 16 * i + 4 * g4 + v] = m;
+        m = fmaxf(m, fabsf(h[i][v]));
       }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (g4 == 0) red[wave * FS_TBM + 16 * i + c16] = m;
     }
     __syncthreads();
-    const int col = nt * 128 + 16 * wave + c16;
+    const int col = nt * 128 + 16 * wave + 4 * g4;
 #pragma unroll
     for (int i = 0; i < FS_RB; ++i) {
       if (2 * mact <= i) continue;
+      const int r = 16 * i + c16;
+      float amax = 0.f;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 16 * i + 4 * g4 + v;
-        float amax = 0.f;
+      for (int w = 0; w < FS_NWAVE; ++w) amax = fmaxf(amax, red[w * FS_TBM + r]);
+      const float scale = e4m3_scale(amax);
+      uint32_t codes = 0;
 #pragma unroll
-        for (int w = 0; w < FS_NWAVE; ++w) amax = fmaxf(amax, red[w * FS_TBM + r]);
-        const float scale = e4m3_scale(amax);
-        if (r < rows) {
-          const size_t orow = (size_t)(row_base + m0 + r);
-          g.out8[orow * g.N + col] = uint8_t(e4m3_encode(h[i][v] / scale));
-          if (wave == 0 && c16 == 0) g.out_s[orow * NB + nt] = scale;
-        }
+      for (int v = 0; v < 4; ++v) codes |= e4m3_encode(h[i][v] / scale) << (8 * v);
+      if (r < rows) {
+        const size_t orow = (size_t)(row_base + m0 + r);
+        *reinterpret_cast<uint32_t*>(g.out8 + orow * g.N + col) = codes;
+        if (wave == 0 && g4 == 0) g.out_s[orow * NB + nt] = scale;
       }
     }
   } else {
@@ -403,11 +432,12 @@ __global__ __launch_bounds__(FS_NTHREAD, 1) void tile_gemm_fp8_kernel(TileArgs8 
     for (int i = 0; i < FS_RB; ++i) {
       if (2 * mact <= i) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          *(__attribute__((address_space(3))) bf16_t*)(stg + (4 * g4 + v) * PITCH + 2 * (16 * j + c16)) =
-              f32_to_bf16(acc[i][j][v]);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t p0 = uint32_t(f32_to_bf16(acc[i][j][0])) | (uint32_t(f32_to_bf16(acc[i][j][1])) << 16);
+        const uint32_t p1 = uint32_t(f32_to_bf16(acc[i][j][2])) | (uint32_t(f32_to_bf16(acc[i][j][3])) << 16);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *(__attribute__((address_space(3))) u32x2*)(stg + c16 * PITCH + 2 * (16 * j + 4 * g4)) = u32x2{p0, p1};
+      }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const int rr = lane >> 2, cb = 16 * (lane & 3);
       const u32x4 val = *(__attribute__((address_space(3))) const u32x4*)(stg + rr * PITCH + cb);
