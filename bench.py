@@ -4,6 +4,7 @@
     python bench.py --workload fp8 --save-inputs DIR   # write the inputs, then ...
     python bench.py --workload fp8 --load-inputs DIR   # ... time them without generator kernels
     python bench.py --copy-calibration          # plain copy of known size, for HBM counters
+    python bench.py --matmul-calibration        # a large library bf16 GEMM, for MFMA counters
     python bench.py --summarize-profile DIR     # text summary of rocprofv3 CSV output
 
 A step is one moe_forward call (router, node-limited top-8 selection, gates,
@@ -48,25 +49,31 @@ COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buff
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
     "decode": {"src_sha256": "c958487bd206fb3715457dc850ca5415a567a010a08736def4e085277c001ae9",
              "fetch_kib": 7495490.2, "write_kib": 9216.0},
-    "fp8": {"src_sha256": "4fd6e2e96886b83d35f9622100f1a7238812d9c3f0fddd18a8a2400198295c9d",
-            "fetch_kib": 4964611.9, "write_kib": 92203.6},
-    "prefill": {"src_sha256": "ee4cbfbbd3dcd9296fc1252514015ba2e84d5ede317bbd733ff4bd876784c30a",
-              "fetch_kib": 12196422.0, "write_kib": 294912.0},
-    "backward_prefill_bf16": {"src_sha256": "e1b37b1c6ff208e6636a40082ff83313615a61301e54f45334c9305577a7016b",
-                            "fetch_kib": 6421738.9, "write_kib": 44214469.8},
-    "backward_decode_bf16": {"src_sha256": "e1b37b1c6ff208e6636a40082ff83313615a61301e54f45334c9305577a7016b",
-                            "fetch_kib": 85693.1, "write_kib": 44233619.9},
+    "fp8": {"src_sha256": "c822c9dd7123469678895a1f6061579bac09842b8efefe65869e038743180275",
+            "fetch_kib": 4913502.7, "write_kib": 92287.6},
+    "prefill": {"src_sha256": "1ac11f9511b0b11041b32f49324db9dc9f294cef5f6f87b53eadb89a3fda63a1",
+              "fetch_kib": 12246336.4, "write_kib": 294912.0},
+    "backward_prefill_bf16": {"src_sha256": "a316b73a9d8f0e12abe357db6ff680cee9dc65e8519bd702c4e7a888b8f6bd44",
+                            "fetch_kib": 6416538.5, "write_kib": 44214805.0},
+    "backward_decode_bf16": {"src_sha256": "a316b73a9d8f0e12abe357db6ff680cee9dc65e8519bd702c4e7a888b8f6bd44",
+                            "fetch_kib": 85694.1, "write_kib": 44232560.8},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F8, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "ee4cbfbbd3dcd9296fc1252514015ba2e84d5ede317bbd733ff4bd876784c30a",
-                "busy": 0.576, "clock_ghz": 1.54, "executed_bf16_tflop": 4.56},
+    "prefill": {"src_sha256": "1ac11f9511b0b11041b32f49324db9dc9f294cef5f6f87b53eadb89a3fda63a1",
+                "busy": 0.591, "clock_ghz": 1.51, "executed_bf16_tflop": 4.56},
     # (SQ_INSTS_VALU_MFMA_MOPS_F8; profiles/moe_forward_fp8_e4m3.md)
-    "fp8": {"src_sha256": "4fd6e2e96886b83d35f9622100f1a7238812d9c3f0fddd18a8a2400198295c9d",
-            "busy": 0.234, "clock_ghz": 1.96, "executed_f8_tflop": 2.40},
+    "fp8": {"src_sha256": "c822c9dd7123469678895a1f6061579bac09842b8efefe65869e038743180275",
+            "busy": 0.312, "clock_ghz": 1.88, "executed_f8_tflop": 2.40},
 }
+# A plain 8192 x 8192 x 7168 bf16 GEMM through torch.matmul (hipBLASLt), `--matmul-calibration`,
+# with its MFMA counters (profiles/moe_forward_prefill_bf16.md): what the vendor library sustains
+# on this part on an ideal shape, at the clock the chip held under it.  Independent of this
+# library's sources.
+MATMUL_REFERENCE = {"kernel": "hipBLASLt bf16 GEMM 8192x8192x7168 (torch.matmul)",
+                    "tflops_timed": 1164.0, "mfma_busy": 0.696, "clock_ghz": 1.70}
 # sources the gate/up kernel of each workload is built and launched from
 _COMMON_SOURCES = ("common.h", "kernels.h", "moe_api.cpp")
 KERNEL_SOURCES = {"decode": _COMMON_SOURCES + ("lds_async.h", "stream_gemm.hip"),
@@ -128,6 +135,32 @@ def copy_calibration(reps=5, nbytes=1 << 30):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
                                             "reps": reps, "forms": ["copy_", "neg"]}}), flush=True)
+
+
+def matmul_calibration(reps=20, m=8192, n=8192, k=7168):
+    """A large plain bf16 GEMM through torch (hipBLASLt): what the vendor library
+    sustains on this part, and, under rocprofv3 --pmc, the MFMA busy fraction and
+    the clock the chip holds under a dense MFMA load."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(m, k, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(k, n, device=dev, dtype=torch.bfloat16, generator=g)  # contiguous, plain 2-D mm
+    c = torch.empty(m, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    flops = 2.0 * m * n * k
+    print(json.dumps({"matmul_calibration": {"m": m, "n": n, "k": k, "dtype": "bf16", "reps": reps,
+                                             "ms": round(ms, 4),
+                                             "tflops": round(flops / ms / 1e9, 1)}}), flush=True)
 
 
 def summarize_profile(path):
@@ -208,6 +241,8 @@ def main():
                          "of generating them: the process then dispatches no generator kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run plain copies of known size (for HBM counter calibration) and exit")
+    ap.add_argument("--matmul-calibration", action="store_true",
+                    help="time a large library bf16 GEMM (for MFMA counter reference) and exit")
     ap.add_argument("--summarize-profile", default=None, metavar="DIR",
                     help="print a text summary of the rocprofv3 CSV files under DIR and exit")
     args = ap.parse_args()
@@ -234,6 +269,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.matmul_calibration:
+        matmul_calibration()
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -405,6 +443,7 @@ def bench_forward(name, args, np, torch, moe, S, dev, primary):
                 "alg_bytes_per_launch": int(gu_bytes), "alg_flops_per_launch": int(gu_flops)}
     if bound == "mfma":
         roofline["mfma_counters"] = measured_mfma(c.name)
+        roofline["library_gemm_reference"] = MATMUL_REFERENCE
     if c.w_dtype == "e4m3":   # the same kernel against the fp8 matrix cores
         roofline["mfma_frac_e4m3"] = round(gu_flops / gu_s / 1e12 / MFMA_PEAK_TFLOPS["e4m3"], 4)
         roofline["mfma_counters"] = measured_mfma(c.name)
