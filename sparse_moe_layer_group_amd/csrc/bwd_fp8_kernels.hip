@@ -28,6 +28,8 @@
 // gradients are written transposed: per expert e, [C][Kp_e] codes with Kp_e =
 // its rows rounded up to 128 (zero codes past its last row) and [C][Kp_e/128]
 // scales.
+#include <type_traits>
+
 #include "bwd.h"
 #include "common.h"
 #include "lds_async.h"
@@ -256,58 +258,98 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
     return i32x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
   };
 
-  if (steps > 0) issue(0);
-  for (int step = 0; step < steps; ++step) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies of step landed
-    __syncthreads();                     // everyone's; everyone is done with step - 1
-    if (step + 1 < steps) issue(step + 1);
-    const uint8_t* st = smem + (step % F8_NS) * F8_STAGE;
-    const float* scA = reinterpret_cast<const float*>(st + 2 * F8_OP);
-    const float* scB = scA + F8_T;
-    float sbb = 1.f;
-    if (GROUP == 0) {
-      const bool s1 = NSRC == 2 && step >= KB;
-      const int kb = s1 ? step - KB : step;
-      const float v = kb < 64 ? sbv[s1 ? NSRC - 1 : 0][0] : sbv[s1 ? NSRC - 1 : 0][1];
-      sbb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
-    }
-    i32x8 bf[4];
-    float sbj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf[j] = BN ? frag_kn(st + F8_OP, 64 * wn + 16 * j) : frag(st + F8_OP, 64 * wn + 16 * j + c16);
-      sbj[j] = GROUP == 0 ? sbb : scB[64 * wn + 16 * j + c16];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= rb_act) continue;  // uniform
-      const i32x8 af = frag(st, 64 * wm + 16 * i + c16);
-      const f32x4 sa = *reinterpret_cast<const f32x4*>(scA + 64 * wm + 16 * i + 4 * g4);
+  // One K step of NRB active row blocks.  The weight-side fragment is the
+  // MFMA's first operand, so a lane's four results of a block are four
+  // adjacent columns of one row: GROUP 0 promotes them with one scale
+  // product per row block.  The MFMA of pair p + 1 is issued before the
+  // promotion of pair p, so the vector ALU works while the matrix core does;
+  // all of the step's fragments are read up front.
+  auto step_body = [&](int step, auto nrb_c) {
+    constexpr int NRB = decltype(nrb_c)::value;
+    if constexpr (NRB > 0) {
+      const uint8_t* st = smem + (step % F8_NS) * F8_STAGE;
+      const float* scA = reinterpret_cast<const float*>(st + 2 * F8_OP);
+      const float* scB = scA + F8_T;
+      float sbb = 1.f;
+      if (GROUP == 0) {
+        const bool s1 = NSRC == 2 && step >= KB;
+        const int kb = s1 ? step - KB : step;
+        const float v = kb < 64 ? sbv[s1 ? NSRC - 1 : 0][0] : sbv[s1 ? NSRC - 1 : 0][1];
+        sbb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
+      }
+      i32x8 bf[4];
+      f32x4 sbq[4];  // GROUP 1: the scales of the lane's four columns of block j
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 t =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], zero, 0, 0, 0, 127, 0, 127);
+        bf[j] = BN ? frag_kn(st + F8_OP, 64 * wn + 16 * j) : frag(st + F8_OP, 64 * wn + 16 * j + c16);
+        if (GROUP == 1) sbq[j] = *reinterpret_cast<const f32x4*>(scB + 64 * wn + 16 * j + 4 * g4);
+      }
+      i32x8 af[NRB];
+      float sa[NRB];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(t[v], sa[v] * sbj[j], acc[i][j][v]);
+      for (int i = 0; i < NRB; ++i) {
+        af[i] = frag(st, 64 * wm + 16 * i + c16);
+        sa[i] = scA[64 * wm + 16 * i + c16];
+      }
+      constexpr int P = 4 * NRB;
+      f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[0], af[0], zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int i = p >> 2, j = p & 3;
+        f32x4 u = zero;
+        if (p + 1 < P)
+          u = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[(p + 1) & 3], af[(p + 1) >> 2], zero, 0, 0,
+                                                               0, 127, 0, 127);
+        if (GROUP == 0) {
+          const float sc = sa[i] * sbb;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(t[v], sc, acc[i][j][v]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(t[v], sa[i] * sbq[j][v], acc[i][j][v]);
+        }
+        if (p + 1 < P) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // the next MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, GROUP == 0 ? 4 : 8, 0);  // this promotion
+        }
+        t = u;
       }
     }
+  };
+  auto mainloop = [&](auto nrb_c) {
+    if (steps > 0) issue(0);
+    for (int step = 0; step < steps; ++step) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies of step landed
+      __syncthreads();                     // everyone's; everyone is done with step - 1
+      if (step + 1 < steps) issue(step + 1);
+      step_body(step, nrb_c);
+    }
+  };
+  switch (rb_act) {
+    case 4: mainloop(std::integral_constant<int, 4>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    default: mainloop(std::integral_constant<int, 0>{}); break;
   }
 
-  // ---- epilogue.  16x16 accumulator v of lane l: row 4 (l/16) + v, column l%16
+  // ---- epilogue.  16x16 accumulator v of lane l: row l%16, column 4 (l/16) + v
   if (GROUP == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= rb_act) continue;
+      const int r = 64 * wm + 16 * i + c16;
+      if (r >= rows) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + c16;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = 64 * wm + 16 * i + 4 * g4 + v;
-          if (r < rows) {
-            TO* o = static_cast<TO*>(g.out) + (size_t)(row_base + m0 + r) * g.N + n;
-            *o = from_f32<TO>(acc[i][j][v]);
-          }
+        TO* o = static_cast<TO*>(g.out) + (size_t)(row_base + m0 + r) * g.N + n0 + 64 * wn + 16 * j + 4 * g4;
+        if constexpr (std::is_same<TO, float>::value) {
+          *reinterpret_cast<f32x4*>(o) = acc[i][j];
+        } else {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const uint32_t p0 = uint32_t(from_f32<TO>(acc[i][j][0])) | (uint32_t(from_f32<TO>(acc[i][j][1])) << 16);
+          const uint32_t p1 = uint32_t(from_f32<TO>(acc[i][j][2])) | (uint32_t(from_f32<TO>(acc[i][j][3])) << 16);
+          *reinterpret_cast<u32x2*>(o) = u32x2{p0, p1};
         }
       }
     }
@@ -325,9 +367,7 @@ __global__ __launch_bounds__(F8_NT, 2) void f8_gemm_kernel(F8GemmArgs g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          tile[(64 * wm + 16 * i + 4 * g4 + v) * LD + 64 * wn + 16 * j + c16] = acc[i][j][v];
+        *reinterpret_cast<f32x4*>(tile + (64 * wm + 16 * i + c16) * LD + 64 * wn + 16 * j + 4 * g4) = acc[i][j];
     __syncthreads();
     float* out = static_cast<float*>(g.out) + ((size_t)e * g.M + m0) * g.N + n0;
 #pragma unroll
