@@ -68,8 +68,8 @@ class ExpertsAhead:
 class V3Run:
     """One GPU forward of a V3-shaped workload and what the oracle needs."""
 
-    def __init__(self, name):
-        c = S.get_config(name)
+    def __init__(self, name, cfg=None):
+        c = S.get_config(name) if cfg is None else cfg
         self.c = c
         say(f"V3 {name}: GPU forward (T={c.T})")
         gi = GpuInputs(c)          # step 0 of the workload (its initial bias)
