@@ -147,10 +147,11 @@ def test_backward_with_an_underflowed_gate():
         assert float(got[e0].abs().max()) == 0.0 and float(np.abs(want).max()) < 1e-40
 
 
+@pytest.mark.parametrize("seed", [None, 21])   # the workload's own seed, and one more
 @pytest.mark.parametrize("name", ["decode", "prefill"])
-def test_v3_backward_sampled(name):
-    c = S.get_config(name)
-    say(f"V3 backward {name}: T={c.T}")
+def test_v3_backward_sampled(name, seed):
+    c = S.get_config(name) if seed is None else S.get_config(name, seed=seed)
+    say(f"V3 backward {name}: T={c.T}, seed {c.seed}")
     gi = GpuInputs(c)
     dy = _dy(c)
     dx, dwr, dwg, dwu, dwd = _run(gi, dy)

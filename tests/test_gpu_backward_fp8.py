@@ -102,9 +102,10 @@ def test_fp8_backward_is_deterministic():
         assert torch.equal(u, v)
 
 
-def test_v3_fp8_backward_sampled():
-    c = S.get_config("fp8", T=256)
-    say(f"V3 fp8 backward: T={c.T}")
+@pytest.mark.parametrize("seed", [None, 21])   # the workload's own seed, and one more
+def test_v3_fp8_backward_sampled(seed):
+    c = S.get_config("fp8", T=256) if seed is None else S.get_config("fp8", T=256, seed=seed)
+    say(f"V3 fp8 backward: T={c.T}, seed {c.seed}")
     gi = GpuInputs(c)
     dy = _dy(c)
     out = _run(gi, dy)
