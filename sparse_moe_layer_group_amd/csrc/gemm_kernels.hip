@@ -194,8 +194,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs<TE> g) {
 // Gated combine: y[t] = sum_s Y[TK + s*T + t] + sum_k gate[t][k] * Y[slot[t*K+k]]
 // (+ residual), float32 accumulation, shared experts first then k ascending
 // (the chosen ids ascend).  A 128-thread block covers 128 16-byte vectors of
-// one token row (grid: tokens x column blocks), so every thread issues all of
-// its K + S + 1 loads at once.
+// one token row, so every thread issues all of its K + S + 1 loads at once.
+// The grid is one-dimensional with a token's column blocks adjacent, so the
+// blocks that run together read whole rows of the staged outputs.
 // ============================================================================
 
 constexpr int COMBINE_THREADS = 128;
@@ -206,9 +207,9 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const TE* __re
                                                       const float* __restrict__ gate,
                                                       const TE* __restrict__ residual,
                                                       TE* __restrict__ y, int T, int K, int H,
-                                                      int TK, int S) {
+                                                      int TK, int S, int ncb) {
   constexpr int CE = 16 / sizeof(TE);
-  const int t = blockIdx.x;
+  const int t = int(blockIdx.x / unsigned(ncb)), cb = int(blockIdx.x - unsigned(t) * unsigned(ncb));
   __shared__ int rows_s[33];
   __shared__ float g_s[33];
   if (threadIdx.x < K) {
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const TE* __re
     g_s[threadIdx.x] = gate[(size_t)t * K + threadIdx.x];
   }
   __syncthreads();
-  const int c = (blockIdx.y * COMBINE_THREADS + threadIdx.x) * CE;
+  const int c = (cb * COMBINE_THREADS + threadIdx.x) * CE;
   if (c < H) {  // H % 128 == 0: whole vectors
     float acc[CE];
 #pragma unroll
@@ -274,8 +275,11 @@ hipError_t launch_combine(const TE* Y, const int32_t* slot, const float* gate, c
                           TE* y, int T, int K, int H, int TK, int S, hipStream_t st) {
   constexpr int CE = 16 / sizeof(TE);
   const int ncb = (H / CE + COMBINE_THREADS - 1) / COMBINE_THREADS;
-  hipLaunchKernelGGL(combine_kernel<TE>, dim3(T, ncb), dim3(COMBINE_THREADS), 0, st, Y, slot, gate,
-                     residual, y, T, K, H, TK, S);
+  const long long blocks = (long long)T * ncb;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel<TE>, dim3((unsigned)blocks), dim3(COMBINE_THREADS), 0, st, Y,
+                     slot, gate, residual, y, T, K, H, TK, S, ncb);
   return hipGetLastError();
 }
 

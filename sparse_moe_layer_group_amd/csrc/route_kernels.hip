@@ -522,11 +522,29 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                    int32_t* __restrict__ offsets, int stream_max,
                                                    int32_t* __restrict__ chunk_start, int bm,
                                                    int32_t* __restrict__ mt_start) {
+  constexpr int QMAX = 8;
   __shared__ int wave_tot[16];
+  __shared__ int part_s[QMAX][SEL_MAX_E];  // per expert: chunk counts of each thread's range
+  __shared__ int off_s[SEL_MAX_E];
+  // Q threads per expert (as many as the block holds, at most QMAX): thread
+  // (q, ex) covers the contiguous chunks [c0, c1) of expert ex, so every
+  // thread has few chunks, and the unrolled loops issue their independent
+  // loads together (one thread walking all chunks waited on them serially)
+  const int Q = min(QMAX, int(blockDim.x) / E);
+  const int ex = threadIdx.x % E, q = threadIdx.x / E;
+  const bool part = q < Q;
+  const int c0 = part ? int((long long)q * nchunks / Q) : 0;
+  const int c1 = part ? int((long long)(q + 1) * nchunks / Q) : 0;
+  int psum = 0;
+#pragma unroll 8
+  for (int c = c0; c < c1; ++c) psum += hist[(size_t)c * E + ex];
+  if (part) part_s[q][ex] = psum;
+  __syncthreads();
+
   const int e = threadIdx.x;  // blockDim.x >= E + S + 1
   int cnt = 0;
   if (e < E)
-    for (int c = 0; c < nchunks; ++c) cnt += hist[(size_t)c * E + e];
+    for (int i = 0; i < Q; ++i) cnt += part_s[i][e];
   // rows of entry e of the work tables: routed experts, then the shared ones
   const int rows = e < E ? cnt : (e < E + S ? T : 0);
   const bool str = rows <= stream_max;
@@ -537,16 +555,25 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (e < E) {
     counts[e] = cnt;
     offsets[e] = off;
-    int run = off;
-    for (int c = 0; c < nchunks; ++c) {
-      base[(size_t)c * E + e] = run;
-      run += hist[(size_t)c * E + e];
-    }
+    off_s[e] = off;
   }
   if (e == E) offsets[E] = off;
   if (e <= E + S) {
     chunk_start[e] = sa;
     mt_start[e] = sb;
+  }
+  __syncthreads();
+  // each chunk's first row per expert: the expert's offset plus the rows of
+  // its earlier chunks
+  if (part) {
+    int run = off_s[ex];
+    for (int i = 0; i < q; ++i) run += part_s[i][ex];
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
+      const int h = hist[(size_t)c * E + ex];
+      base[(size_t)c * E + ex] = run;
+      run += h;
+    }
   }
 }
 
