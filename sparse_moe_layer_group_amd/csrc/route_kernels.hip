@@ -318,14 +318,45 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ P
   float* z = z_s[wave];
   float* s = s_s[wave];
 
-  for (int j = 0; j < epl; ++j) {
-    int e = lane * epl + j;
-    if (e < E) {
-      float L = 0.f;
-      for (int k = 0; k < ksplit; ++k) L += P[((size_t)k * T + t) * E + e];
-      float sv = sigmoidf(L);
-      s[e] = sv;
-      z[e] = sv + bias[e];
+  {
+    // logits: each expert's partials summed in ascending k.  Lane l reads
+    // experts l, l + 64, ... (coalesced), four partials of each at a time, so
+    // a token's loads are in flight together rather than one after another.
+    float Lv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Lv[j] = 0.f;
+    const float* Pt = P + (size_t)t * E;
+    const size_t kst = (size_t)T * E;
+    int k = 0;
+    for (; k + 4 <= ksplit; k += 4) {
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = 64 * j + lane;
+          v[q][j] = (j < epl && e < E) ? Pt[(size_t)(k + q) * kst + e] : 0.f;
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Lv[j] += v[q][j];
+    }
+    for (; k < ksplit; ++k) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 64 * j + lane;
+        if (j < epl && e < E) Lv[j] += Pt[(size_t)k * kst + e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = 64 * j + lane;
+      if (j < epl && e < E) {
+        const float sv = sigmoidf(Lv[j]);
+        s[e] = sv;
+        z[e] = sv + bias[e];
+      }
     }
   }
   __syncthreads();
