@@ -196,7 +196,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs<TE> g) {
 // (the chosen ids ascend).  A 128-thread block covers 128 16-byte vectors of
 // one token row, so every thread issues all of its K + S + 1 loads at once.
 // The grid is one-dimensional with a token's column blocks adjacent, so the
-// blocks that run together read whole rows of the staged outputs.
+// blocks that run together read whole rows of the staged outputs.  Staged
+// rows are read once and y written once: both non-temporal (at 8192 tokens
+// 231 -> 184 us, at 4096 tokens with E4M3 weights 124 -> 90 us).
 // ============================================================================
 
 constexpr int COMBINE_THREADS = 128;
@@ -224,14 +226,14 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const TE* __re
     for (int q = 0; q < CE; ++q) acc[q] = 0.f;
     for (int sh = 0; sh < S; ++sh) {
       const TE* src = Y + (size_t)(TK + sh * T + t) * H + c;
-      u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
       const TE* pv = reinterpret_cast<const TE*>(&v);
 #pragma unroll
       for (int q = 0; q < CE; ++q) acc[q] += to_f32<TE>(pv[q]);
     }
     for (int k = 0; k < K; ++k) {
       const float gk = g_s[k];
-      u32x4 v = *reinterpret_cast<const u32x4*>(Y + (size_t)rows_s[k] * H + c);
+      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Y + (size_t)rows_s[k] * H + c));
       const TE* pv = reinterpret_cast<const TE*>(&v);
 #pragma unroll
       for (int q = 0; q < CE; ++q) acc[q] = fmaf(gk, to_f32<TE>(pv[q]), acc[q]);
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const TE* __re
     TE* po = reinterpret_cast<TE*>(&o);
 #pragma unroll
     for (int q = 0; q < CE; ++q) po[q] = from_f32<TE>(acc[q]);
-    *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(y + (size_t)t * H + c));
   }
 }
 
