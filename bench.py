@@ -53,10 +53,10 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
             "fetch_kib": 4913502.7, "write_kib": 92287.6},
     "prefill": {"src_sha256": "1ac11f9511b0b11041b32f49324db9dc9f294cef5f6f87b53eadb89a3fda63a1",
               "fetch_kib": 12246336.4, "write_kib": 294912.0},
-    "backward_prefill_bf16": {"src_sha256": "a316b73a9d8f0e12abe357db6ff680cee9dc65e8519bd702c4e7a888b8f6bd44",
-                            "fetch_kib": 6416538.5, "write_kib": 44214805.0},
-    "backward_decode_bf16": {"src_sha256": "a316b73a9d8f0e12abe357db6ff680cee9dc65e8519bd702c4e7a888b8f6bd44",
-                            "fetch_kib": 85694.1, "write_kib": 44232560.8},
+    "backward_prefill_bf16": {"src_sha256": "2128ce0fa66e0506a9238675fc3ef127e496b8b08d0243b59df5b3c91fa379b5",
+                            "fetch_kib": 6459360.2, "write_kib": 44215141.9},
+    "backward_decode_bf16": {"src_sha256": "2128ce0fa66e0506a9238675fc3ef127e496b8b08d0243b59df5b3c91fa379b5",
+                            "fetch_kib": 85689.9, "write_kib": 44234533.9},
 }
 # MFMA counters of gemm_gate_up from one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES,
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F8, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):

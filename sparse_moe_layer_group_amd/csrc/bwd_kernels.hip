@@ -1048,25 +1048,42 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   }
 }
 
-// dW_r^T[e][h] = sum over expert e's routed rows r of dL_r X_r[h], rows in order
+// dW_r^T[e][h] = sum over expert e's routed rows r of dL_r X_r[h], rows in order.
+// X_r is token perm[r]'s row of x, read through the permutation (x is small
+// enough to stay in the caches, its staged copy is not); eight rows' loads are
+// issued together and added in row order.
 __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dlst,
-                                                  const bf16_t* __restrict__ xst,
+                                                  const bf16_t* __restrict__ x,
+                                                  const int32_t* __restrict__ perm,
                                                   const int32_t* __restrict__ counts,
                                                   const int32_t* __restrict__ offsets, int H,
                                                   float* __restrict__ dwrt) {
+  constexpr int U = 8;
   const int e = blockIdx.x;
   const int h = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (h >= H) return;
   const int base = offsets[e], cnt = counts[e];
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int r = 0; r < cnt; ++r) {
-    const float w = dlst[base + r];
-    const uint2 v = *reinterpret_cast<const uint2*>(xst + size_t(base + r) * H + h);
+  auto add = [&](float w, uint2 v) {
     a0 = fmaf(w, __uint_as_float(v.x << 16), a0);
     a1 = fmaf(w, __uint_as_float(v.x & 0xffff0000u), a1);
     a2 = fmaf(w, __uint_as_float(v.y << 16), a2);
     a3 = fmaf(w, __uint_as_float(v.y & 0xffff0000u), a3);
+  };
+  int r = 0;
+  for (; r + U <= cnt; r += U) {
+    float w[U];
+    uint2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w[u] = dlst[base + r + u];
+      v[u] = *reinterpret_cast<const uint2*>(x + size_t(perm[base + r + u]) * H + h);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) add(w[u], v[u]);
   }
+  for (; r < cnt; ++r)
+    add(dlst[base + r], *reinterpret_cast<const uint2*>(x + size_t(perm[base + r]) * H + h));
   *reinterpret_cast<f32x4*>(dwrt + size_t(e) * H + h) = f32x4{a0, a1, a2, a3};
 }
 
@@ -1084,37 +1101,65 @@ __global__ __launch_bounds__(256) void transpose_f32_kernel(const float* __restr
 }
 
 // dx_t = dX_shared[t] + sum_k dX[slot(t, k)] + sum_k dL_tk W_r[:, e_k], float32
-// in that order, bf16 out
+// in that order, bf16 out.  The token's slots, expert ids and logit gradients
+// sit in LDS, and the rows of each group of up to eight terms are loaded
+// together before they are added in order.
 __global__ __launch_bounds__(256) void dx_kernel(const bf16_t* __restrict__ dxst,
                                                  const int32_t* __restrict__ slot,
                                                  const int32_t* __restrict__ idx,
                                                  const float* __restrict__ dl,
                                                  const float* __restrict__ wrt, int T, int K,
                                                  int H, int TK, int S, bf16_t* __restrict__ dx) {
+  constexpr int U = 8;
+  __shared__ int sl_s[32], ix_s[32];
+  __shared__ float dl_s[32];
   const int t = blockIdx.x;
+  if (threadIdx.x < K) {
+    sl_s[threadIdx.x] = slot[t * K + threadIdx.x];
+    ix_s[threadIdx.x] = idx[t * K + threadIdx.x];
+    dl_s[threadIdx.x] = dl[t * K + threadIdx.x];
+  }
+  __syncthreads();
   for (int c = threadIdx.x; c < H / 8; c += 256) {
     float a[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) a[q] = 0.f;
-    auto add_row = [&](size_t row) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(dxst + row * H)[c];
+    auto add_row = [&](const u32x4& v) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         a[2 * q] += __uint_as_float(v[q] << 16);
         a[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
       }
     };
-    if (S > 0) add_row(size_t(TK + t));
-    for (int k = 0; k < K; ++k) add_row(size_t(slot[t * K + k]));
-    for (int k = 0; k < K; ++k) {
-      const float w = dl[t * K + k];
-      const f32x4* r = reinterpret_cast<const f32x4*>(wrt + size_t(idx[t * K + k]) * H + 8 * c);
-      const f32x4 r0 = r[0], r1 = r[1];
+    if (S > 0) add_row(reinterpret_cast<const u32x4*>(dxst + size_t(TK + t) * H)[c]);
+    for (int k0 = 0; k0 < K; k0 += U) {
+      u32x4 v[U];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a[q] = fmaf(w, r0[q], a[q]);
-        a[4 + q] = fmaf(w, r1[q], a[4 + q]);
-      }
+      for (int u = 0; u < U; ++u)
+        if (k0 + u < K) v[u] = reinterpret_cast<const u32x4*>(dxst + size_t(sl_s[k0 + u]) * H)[c];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k0 + u < K) add_row(v[u]);
+    }
+    for (int k0 = 0; k0 < K; k0 += U) {
+      f32x4 r0[U], r1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k0 + u < K) {
+          const f32x4* r = reinterpret_cast<const f32x4*>(wrt + size_t(ix_s[k0 + u]) * H + 8 * c);
+          r0[u] = r[0];
+          r1[u] = r[1];
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k0 + u < K) {
+          const float w = dl_s[k0 + u];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a[q] = fmaf(w, r0[u][q], a[q]);
+            a[4 + q] = fmaf(w, r1[u][q], a[4 + q]);
+          }
+        }
     }
     u32x4 o;
 #pragma unroll
@@ -1241,8 +1286,8 @@ hipError_t launch_backward_kernels(const BwdArgs& g, const float* P, int ks, con
       break;
     }
     case 7:  // router weight gradient: dW_r^T per expert, then transposed
-      hipLaunchKernelGGL(dwr_kernel, dim3(E, (H / 4 + 255) / 256), dim3(256), 0, st, g.dlst, g.xst,
-                         g.counts, g.offsets, H, g.dwrt);
+      hipLaunchKernelGGL(dwr_kernel, dim3(E, (H / 4 + 255) / 256), dim3(256), 0, st, g.dlst, g.x,
+                         g.perm, g.counts, g.offsets, H, g.dwrt);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       hipLaunchKernelGGL(transpose_f32_kernel, dim3((H + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
                          g.dwrt, E, H, dw_router);

@@ -415,7 +415,6 @@ BwdLayout make_bwd_layout(const moe_cfg& c, int64_t T) {
     const size_t n = E + S, HB = H / 128, IB = I / 128;
     // 128x1 operands: each expert's rows rounded up to 128
     const size_t rcap = 128 * size_t(moe::f8_max_row_tiles(int(T), int(K), int(E), int(S)));
-    B.xst = take(rows * H * 2);
     B.f32a = take(rows * I * 4);
     B.f32b = take(rows * I * 4);
     B.gq = take(rows * I);
@@ -667,7 +666,6 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
   g.counts = r.counts;
   g.offsets = r.offsets;
   g.mt = at<int32_t>(ws, B.mt);
-  g.xst = at<bf16_t>(ws, B.xst);
   g.yst = at<bf16_t>(ws, L.yst);
   g.dyst = nullptr;  // the output gradients are quantised from float32 instead
   g.dxst = q.dxst;
@@ -696,8 +694,7 @@ int run_backward_fp8(const moe_cfg& c, int T, const bf16_t* x, const float* wr,
     if ((err = moe::launch_quant_1x128(x, T, H, at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), st)) !=
         hipSuccess)
       return err;
-    if ((err = stage8(2)) != hipSuccess) return err;
-    return stage(0);  // x in staged-row order (for dW_r)
+    return stage8(2);
   }));
   MOE_TRY(timed(K_BWD_COMBINE, st, [&]() -> hipError_t {
     hipError_t err;
