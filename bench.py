@@ -47,12 +47,12 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
 COPY_CALIBRATION = {"fetch_bytes_per_kib": 1073741824 / 524302.8,   # 1 GiB buffer copy
                     "write_bytes_per_kib": 1073741824 / 1048576.0}
 MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's kernel
-    "decode": {"src_sha256": "c958487bd206fb3715457dc850ca5415a567a010a08736def4e085277c001ae9",
-             "fetch_kib": 7495490.2, "write_kib": 9216.0},
-    "fp8": {"src_sha256": "c822c9dd7123469678895a1f6061579bac09842b8efefe65869e038743180275",
-            "fetch_kib": 4913502.7, "write_kib": 92287.6},
-    "prefill": {"src_sha256": "1ac11f9511b0b11041b32f49324db9dc9f294cef5f6f87b53eadb89a3fda63a1",
-              "fetch_kib": 12246336.4, "write_kib": 294912.0},
+    "decode": {"src_sha256": "8a0b3e815a6bb8eb2a8c619719e7b54853d7f42ca3b936a329d60aa6b17927ca",
+            "fetch_kib": 7494875.7, "write_kib": 9216.0},
+    "fp8": {"src_sha256": "7274f2c893aa849aefb217607f641dfd9ff36ad1c2c8f306a8a16c7618d02bc9",
+         "fetch_kib": 4913586.8, "write_kib": 92250.3},
+    "prefill": {"src_sha256": "57672187660a41f15929fa5546331706d1b33d8efbc96d9881425f5038d69f06",
+             "fetch_kib": 12248709.7, "write_kib": 294912.1},
     "backward_prefill_bf16": {"src_sha256": "2128ce0fa66e0506a9238675fc3ef127e496b8b08d0243b59df5b3c91fa379b5",
                             "fetch_kib": 6459360.2, "write_kib": 44215141.9},
     "backward_decode_bf16": {"src_sha256": "2128ce0fa66e0506a9238675fc3ef127e496b8b08d0243b59df5b3c91fa379b5",
@@ -62,11 +62,11 @@ MEASURED_TRAFFIC = {         # workload -> counters per launch of the roofline's
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F8, GRBM_GUI_ACTIVE; profiles/moe_forward_prefill_bf16.md):
 # busy = fraction of SIMD-cycles the matrix cores worked at the clock the chip held
 MEASURED_MFMA = {
-    "prefill": {"src_sha256": "1ac11f9511b0b11041b32f49324db9dc9f294cef5f6f87b53eadb89a3fda63a1",
-                "busy": 0.591, "clock_ghz": 1.51, "executed_bf16_tflop": 4.56},
+    "prefill": {"src_sha256": "57672187660a41f15929fa5546331706d1b33d8efbc96d9881425f5038d69f06",
+                "busy": 0.598, "clock_ghz": 1.59, "executed_bf16_tflop": 4.56},
     # (SQ_INSTS_VALU_MFMA_MOPS_F8; profiles/moe_forward_fp8_e4m3.md)
-    "fp8": {"src_sha256": "c822c9dd7123469678895a1f6061579bac09842b8efefe65869e038743180275",
-            "busy": 0.312, "clock_ghz": 1.88, "executed_f8_tflop": 2.40},
+    "fp8": {"src_sha256": "7274f2c893aa849aefb217607f641dfd9ff36ad1c2c8f306a8a16c7618d02bc9",
+            "busy": 0.319, "clock_ghz": 1.94, "executed_f8_tflop": 2.40},
 }
 # A plain 8192 x 8192 x 7168 bf16 GEMM through torch.matmul (hipBLASLt), `--matmul-calibration`,
 # with its MFMA counters (profiles/moe_forward_prefill_bf16.md): what the vendor library sustains
