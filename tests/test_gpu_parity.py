@@ -147,6 +147,8 @@ def test_bias_update_bit_exact_and_skew_steps():
     dict(T=300, n_experts=160, topk=6),                         # 20-expert groups, 3 per lane
     dict(T=2100, n_experts=64),                                 # tiled router, partial tiles
     dict(T=2100, n_experts=512, bias_range=0.5),                # tiled router, large bias
+    dict(T=2100, n_experts=160, topk=6),                        # chunked scan: 6 threads per expert
+    dict(T=1500, n_experts=16, n_groups=4, topk_groups=2, topk=4),  # chunked scan: 8 per expert
     dict(T=1, n_experts=32, n_groups=4, topk_groups=2, topk=4),
 ])
 def test_routing_shapes(kw):
@@ -169,6 +171,7 @@ def test_routing_shapes(kw):
     dict(T=200, topk=1),
     dict(T=300, n_experts=160, topk=6),
     dict(T=2100),                                 # tiled router, tiled GEMMs, 2+ row tiles
+    dict(T=2100, n_experts=160, topk=6),          # chunked scan with 160 experts, tiled GEMMs
 ])
 def test_forward_shapes(kw):
     c = S.get_config("mid").with_(**kw)
